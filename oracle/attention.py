@@ -1,0 +1,249 @@
+"""Plain CPU oracle for batched attention prefill over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, helpers, tables or constants) and imports nothing from it.
+
+Everything here is the plain definition written out, in float64, with NumPy
+matmul / exp / log as the only library steps:
+
+* ``kv_lengths``        -- per-request key count from the paged metadata.
+* ``gather_request_kv`` -- logical K/V rows of one request through its page table.
+* ``allowed_mask``      -- bottom-right causal mask and left-only window.
+* ``attention``         -- masked softmax(sm_scale * Q K^T) V with GQA, plus LSE.
+* ``attention_bruteforce`` -- the same definition as per-element Python loops.
+* ``merge_states`` / ``merge_many`` -- combining partial (o, lse) states.
+
+Sources (web pages of the AMD-Ecosystem FlashInfer fork):
+  [W]  PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
+       section "Why window_size_right stays -1" (left-only, bottom-right
+       anchored band, applied independently of causal).
+  [C]  PR #362 "Support speculative-decode verify on ROCm, and stop auto
+       routing short-query prefill to AITER", Summary and the verify commit
+       message (the ROCm causal mask is bottom-right aligned: the last query
+       row attends to the whole KV).
+  [K]  PR #362, Review notes (kv_len is derived from indptr and
+       last_page_len, not from a caller's seq_lens).
+  [G]  PR #399 "Refuse attention inputs the ROCm kernels would compute
+       wrongly", What changed / GQA head divisibility.
+  [M]  PR #399, What changed / Graph-mode partial_state merge, and PR #362's
+       split-KV test commit (partial (o, lse) states merged into one result).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * kv_len = (n_pages - 1) * page_size + last_page_len, 0 for no pages.
+  * logical key j of a request sits at page indices[indptr[b] + j // P],
+    slot j % P, in an NHD pool [num_pages, P, Hkv, D].
+  * causal keeps j <= i + kv_len - qo_len (bottom-right).
+  * GQA: q head h reads kv head h // (Hq // Hkv) (consecutive groups).
+  * lse uses the natural logarithm.
+  * a row with no visible key has o = 0 and lse = -inf (only reachable for a
+    partial state restricted to a key range).
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(brute force, closed forms, library routines, invariants, golden fixtures).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+def kv_lengths(kv_indptr, kv_last_page_len, page_size):
+    """Per-request key count from the paged metadata [K].
+
+    A request with n >= 1 pages holds (n - 1) full pages plus last_page_len
+    keys on its final page; a request with no page holds no key.
+    """
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    last = np.asarray(kv_last_page_len, dtype=np.int64)
+    n_pages = kv_indptr[1:] - kv_indptr[:-1]
+    return np.where(n_pages > 0, (n_pages - 1) * page_size + last, 0)
+
+
+def gather_request_kv(pool, kv_indptr, kv_page_indices, b, kv_len, page_size):
+    """Logical rows [kv_len, Hkv, D] of request b from an NHD page pool.
+
+    Logical key j lives on physical page kv_page_indices[kv_indptr[b] + j // P]
+    at slot j % P (the paged-KV page table the pages describe for paged_kv_t).
+    """
+    first = int(kv_indptr[b])
+    rows = []
+    for j in range(int(kv_len)):
+        page = int(kv_page_indices[first + j // page_size])
+        rows.append(pool[page, j % page_size])
+    if not rows:
+        return np.zeros((0,) + pool.shape[2:], dtype=np.float64)
+    return np.stack(rows).astype(np.float64)
+
+
+def allowed_mask(qo_len, kv_len, causal, window_left, kv_begin=None, kv_end=None):
+    """Boolean [qo_len, kv_len]: may query row i attend to key j?
+
+    causal [C]: bottom-right aligned, j <= i + kv_len - qo_len.
+    window [W]: left-only band, applied independently of causal,
+                j + qo_len + window_left >= kv_len + i;  window_left = -1
+                means no window.
+    kv_begin/kv_end restrict the keys to [kv_begin, kv_end) in the request's
+    own (global) key coordinates, which is what one split-KV chunk sees [M].
+    """
+    i = np.arange(qo_len, dtype=np.int64)[:, None]
+    j = np.arange(kv_len, dtype=np.int64)[None, :]
+    ok = np.ones((qo_len, kv_len), dtype=bool)
+    if causal:
+        ok &= j <= i + kv_len - qo_len
+    if window_left != -1:
+        ok &= j + qo_len + window_left >= kv_len + i
+    if kv_begin is not None:
+        ok &= j >= kv_begin
+    if kv_end is not None:
+        ok &= j < kv_end
+    return ok
+
+
+def _check_heads(num_qo_heads, num_kv_heads):
+    # [G]: a group size that does not divide the head count is refused.
+    if num_kv_heads <= 0 or num_qo_heads % num_kv_heads != 0:
+        raise ValueError("num_qo_heads must be a positive multiple of num_kv_heads")
+
+
+def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
+              kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
+              window_left, sm_scale, kv_begin=None, kv_end=None):
+    """Masked softmax attention over a paged KV cache, in float64.
+
+    q: [total_q, Hq, D]; k_pool, v_pool: NHD [num_pages, P, Hkv, D].
+    Returns o [total_q, Hq, D] and lse [total_q, Hq] (natural log), both float64.
+    For every request b, q head h, row i:
+        s_ij  = sm_scale * <q_i,h , K_b[j, h // group]>      over allowed j
+        lse_i = log sum_j exp(s_ij)
+        o_i   = sum_j exp(s_ij - lse_i) * V_b[j, h // group]
+    A row with no allowed key gets o = 0, lse = -inf.
+    kv_begin/kv_end (optional) restrict every request to keys in that range of
+    its own key coordinates, giving the partial state of one KV chunk.
+    """
+    _check_heads(num_qo_heads, num_kv_heads)
+    group = num_qo_heads // num_kv_heads
+    q = np.asarray(q, dtype=np.float64)
+    total_q, hq, d = q.shape
+    assert hq == num_qo_heads
+    o = np.zeros((total_q, hq, d), dtype=np.float64)
+    lse = np.full((total_q, hq), NEG_INF, dtype=np.float64)
+    kv_len = kv_lengths(kv_indptr, kv_last_page_len, page_size)
+    for b in range(len(kv_len)):
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        qo_len, L = q1 - q0, int(kv_len[b])
+        if qo_len == 0:
+            continue
+        kb = gather_request_kv(k_pool, kv_indptr, kv_page_indices, b, L, page_size)
+        vb = gather_request_kv(v_pool, kv_indptr, kv_page_indices, b, L, page_size)
+        mask = allowed_mask(qo_len, L, causal, window_left, kv_begin, kv_end)
+        has_key = mask.any(axis=1)
+        for h in range(hq):
+            g = h // group
+            s = sm_scale * (q[q0:q1, h, :] @ kb[:, g, :].T)
+            s = np.where(mask, s, NEG_INF)
+            m = np.max(s, axis=1, initial=NEG_INF)
+            m_safe = np.where(has_key, m, 0.0)
+            e = np.where(mask, np.exp(s - m_safe[:, None]), 0.0)
+            total = e.sum(axis=1)
+            row_lse = np.where(has_key, m_safe + np.log(np.where(has_key, total, 1.0)), NEG_INF)
+            p = e / np.where(has_key, total, 1.0)[:, None]
+            o[q0:q1, h, :] = p @ vb[:, g, :]
+            lse[q0:q1, h] = row_lse
+    return o, lse
+
+
+def attention_bruteforce(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
+                         kv_last_page_len, num_qo_heads, num_kv_heads, page_size,
+                         causal, window_left, sm_scale, kv_begin=None, kv_end=None):
+    """The same definition as ``attention`` as literal per-element loops.
+
+    Pure Python floats (IEEE double), no NumPy arithmetic: for tiny inputs only.
+    Every key's page and slot, the mask predicate and the GQA head are
+    evaluated per (request, head, row, key).
+    """
+    _check_heads(num_qo_heads, num_kv_heads)
+    group = num_qo_heads // num_kv_heads
+    total_q, hq, d = np.shape(q)
+    o = [[[0.0] * d for _ in range(hq)] for _ in range(total_q)]
+    lse = [[NEG_INF] * hq for _ in range(total_q)]
+    batch = len(kv_indptr) - 1
+    for b in range(batch):
+        n_pages = int(kv_indptr[b + 1]) - int(kv_indptr[b])
+        L = 0 if n_pages == 0 else (n_pages - 1) * page_size + int(kv_last_page_len[b])
+        qo_len = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        for h in range(hq):
+            g = h // group
+            for i in range(qo_len):
+                row = int(qo_indptr[b]) + i
+                scores, values = [], []
+                for j in range(L):
+                    ok = True
+                    if causal and not (j <= i + L - qo_len):
+                        ok = False
+                    if window_left != -1 and not (j + qo_len + window_left >= L + i):
+                        ok = False
+                    if kv_begin is not None and j < kv_begin:
+                        ok = False
+                    if kv_end is not None and j >= kv_end:
+                        ok = False
+                    if not ok:
+                        continue
+                    page = int(kv_page_indices[int(kv_indptr[b]) + j // page_size])
+                    slot = j % page_size
+                    dot = 0.0
+                    for t in range(d):
+                        dot += float(q[row][h][t]) * float(k_pool[page][slot][g][t])
+                    scores.append(sm_scale * dot)
+                    values.append([float(v_pool[page][slot][g][t]) for t in range(d)])
+                if not scores:
+                    continue
+                m = max(scores)
+                denom = sum(math.exp(s - m) for s in scores)
+                row_lse = m + math.log(denom)
+                acc = [0.0] * d
+                for s, v in zip(scores, values):
+                    w = math.exp(s - row_lse)
+                    for t in range(d):
+                        acc[t] += w * v[t]
+                o[row][h] = acc
+                lse[row][h] = row_lse
+    return np.array(o, dtype=np.float64).reshape(total_q, hq, d), \
+        np.array(lse, dtype=np.float64).reshape(total_q, hq)
+
+
+def merge_states(o_a, lse_a, o_b, lse_b):
+    """Combine two partial states over disjoint key sets [M].
+
+    If (o_x, lse_x) is softmax attention over key set X, the state over
+    A u B is: lse = log(exp(lse_a) + exp(lse_b)),
+              o   = (exp(lse_a) o_a + exp(lse_b) o_b) / exp(lse).
+    Computed relative to the larger lse; two empty states give (0, -inf).
+    o: [..., D], lse: [...], float64.
+    """
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(lse_a, lse_b)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w_a = np.where(np.isneginf(lse_a), 0.0, np.exp(lse_a - m_safe))
+    w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))
+    total = w_a + w_b
+    denom = np.where(empty, 1.0, total)
+    o = (w_a[..., None] * o_a + w_b[..., None] * o_b) / denom[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, NEG_INF, m_safe + np.log(denom))
+    return o, lse
+
+
+def merge_many(os, lses):
+    """Fold a list of partial states with ``merge_states``, left to right."""
+    o, lse = os[0], lses[0]
+    for o_c, lse_c in zip(os[1:], lses[1:]):
+        o, lse = merge_states(o, lse, o_c, lse_c)
+    return np.asarray(o, dtype=np.float64), np.asarray(lse, dtype=np.float64)

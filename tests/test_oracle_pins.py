@@ -1,0 +1,451 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* hand-derived golden fixtures (tests/golden/),
+* a literal per-element brute force on a grid of tiny inputs,
+* closed forms (K = 0 gives lse = log(#visible keys); V = 1 gives o = 1),
+* library routines (torch scaled_dot_product_attention / logsumexp on CPU),
+* invariants (wide window == no window, GQA == replicated heads, page
+  relabelling, last verify row == decode, split + merge == unsplit),
+* non-vacuity (windowed / causal / GQA variants really differ),
+* planted mistakes: each pin function rejects a deliberately wrong oracle.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers building small random paged problems (float64 values, no rounding)
+# ---------------------------------------------------------------------------
+
+def small_problem(rng, qo_lens, kv_lens, hq, hkv, d, page_size, permute=True):
+    kv_indptr, ids, last, num_pages = workloads.make_page_table(
+        rng, kv_lens, page_size, pool_factor=1.5, permute=permute)
+    qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int64)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+    q = rng.standard_normal((int(qo_indptr[-1]), hq, d))
+    k = rng.standard_normal((num_pages, page_size, hkv, d))
+    v = rng.standard_normal((num_pages, page_size, hkv, d))
+    return dict(q=q, k_pool=k, v_pool=v, qo_indptr=qo_indptr, kv_indptr=kv_indptr,
+                kv_page_indices=ids, kv_last_page_len=last, num_qo_heads=hq,
+                num_kv_heads=hkv, page_size=page_size)
+
+
+def visible_range(i, qo_len, kv_len, causal, window_left):
+    """Inclusive [lo, hi] from the two inequalities, written as integer bounds."""
+    hi = i + kv_len - qo_len if causal else kv_len - 1
+    hi = min(hi, kv_len - 1)
+    lo = 0 if window_left == -1 else max(0, kv_len + i - qo_len - window_left)
+    return lo, hi
+
+
+# ---------------------------------------------------------------------------
+# pin functions (parameterised by the oracle functions so mistakes can be planted)
+# ---------------------------------------------------------------------------
+
+def check_golden_masks(mask_fn):
+    with open(os.path.join(GOLDEN, "mask_ranges.txt")) as f:
+        lines = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) >= 10
+    for ln in lines:
+        head, rows = ln.split("|")
+        qo_len, kv_len, causal, w = (int(t) for t in head.split())
+        want = [tuple(int(x) for x in r.split(",")) for r in rows.split()]
+        got = mask_fn(qo_len, kv_len, bool(causal), w)
+        assert got.shape == (qo_len, kv_len)
+        for i, (lo, hi) in enumerate(want):
+            expect = np.zeros(kv_len, dtype=bool)
+            expect[lo:hi + 1] = True
+            assert np.array_equal(got[i], expect), (ln, i, got[i])
+
+
+def check_golden_attention(attn_fn):
+    with open(os.path.join(GOLDEN, "tiny_attention.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        L, P = c["kv_len"], c["page_size"]
+        n_pages = (L + P - 1) // P
+        k = np.zeros((n_pages, P) + np.shape(c["k"])[1:])
+        v = np.zeros((n_pages, P) + np.shape(c["v"])[1:])
+        for j in range(L):
+            k[j // P, j % P] = c["k"][j]
+            v[j // P, j % P] = c["v"][j]
+        o, lse = attn_fn(np.array(c["q"], dtype=np.float64), k, v,
+                         np.array([0, c["qo_len"]]), np.array([0, n_pages]),
+                         np.arange(n_pages), np.array([L - (n_pages - 1) * P]),
+                         c["num_qo_heads"], c["num_kv_heads"], P, c["causal"],
+                         c["window_left"], c["sm_scale"])
+        np.testing.assert_allclose(o, np.array(c["o"]), rtol=0, atol=1e-12, err_msg=c["name"])
+        np.testing.assert_allclose(lse, np.array(c["lse"]), rtol=0, atol=1e-12, err_msg=c["name"])
+
+
+def check_kv_lengths(kv_len_fn):
+    got = kv_len_fn(np.array([0, 2, 2, 5, 6]), np.array([3, 1, 16, 1]), 16)
+    assert list(got) == [19, 0, 48, 1]
+    assert list(kv_len_fn(np.array([0, 3]), np.array([1]), 1)) == [3]
+
+
+def check_gather(gather_fn):
+    pool = np.zeros((6, 4, 2, 3))
+    for p in range(6):
+        for s in range(4):
+            pool[p, s, :, :] = 100 * p + s
+    indptr = np.array([0, 2, 5])
+    ids = np.array([4, 1, 0, 5, 2])
+    got = gather_fn(pool, indptr, ids, 1, 10, 4)   # request 1: pages 0, 5, 2; 10 keys
+    want = [0, 1, 2, 3, 500, 501, 502, 503, 200, 201]
+    assert np.array_equal(got[:, 0, 0], want)
+
+
+def check_closed_form_k_zero(attn_fn, rng):
+    """K = 0: every visible score is 0, so lse_i = log(n_i), o_i = mean of visible V."""
+    for (qo, kv, causal, w) in [(5, 23, True, -1), (5, 23, True, 3), (7, 19, False, 4),
+                                (1, 40, True, 0), (6, 6, True, 2), (9, 4, False, 1)]:
+        prob = small_problem(rng, [qo], [kv], 4, 2, 8, 5)
+        prob["k_pool"][:] = 0.0
+        o, lse = attn_fn(**prob, causal=causal, window_left=w, sm_scale=0.37)
+        kb = oracle.gather_request_kv  # only to read V rows back out of the pool
+        vb = kb(prob["v_pool"], prob["kv_indptr"], prob["kv_page_indices"], 0, kv, 5)
+        for i in range(qo):
+            lo, hi = visible_range(i, qo, kv, causal, w)
+            n = hi - lo + 1
+            for h in range(4):
+                assert lse[i, h] == pytest.approx(math.log(n), abs=1e-12)
+                want = vb[lo:hi + 1, h // 2, :].mean(axis=0)
+                np.testing.assert_allclose(o[i, h], want, atol=1e-12)
+
+
+def check_v_ones(attn_fn, rng):
+    prob = small_problem(rng, [3, 8, 1], [11, 30, 17], 6, 3, 4, 3)
+    prob["v_pool"][:] = 1.0
+    for causal, w in [(True, -1), (True, 2), (False, 0), (False, -1)]:
+        o, _ = attn_fn(**prob, causal=causal, window_left=w, sm_scale=1.3)
+        np.testing.assert_allclose(o, 1.0, atol=1e-12)
+
+
+def check_sdpa(attn_fn, rng):
+    """Library routine: torch SDPA (float64, CPU) with a mask made by tril/triu."""
+    for (qo, kv, causal, w, hq, hkv) in [(6, 6, True, -1, 2, 2), (5, 17, True, -1, 4, 2),
+                                          (5, 17, True, 3, 4, 1), (8, 13, False, 2, 3, 3),
+                                          (3, 9, False, -1, 2, 1)]:
+        prob = small_problem(rng, [qo], [kv], hq, hkv, 8, 4)
+        o, lse = attn_fn(**prob, causal=causal, window_left=w, sm_scale=0.25)
+        k = torch.from_numpy(oracle.gather_request_kv(prob["k_pool"], prob["kv_indptr"],
+                                                      prob["kv_page_indices"], 0, kv, 4))
+        v = torch.from_numpy(oracle.gather_request_kv(prob["v_pool"], prob["kv_indptr"],
+                                                      prob["kv_page_indices"], 0, kv, 4))
+        q = torch.from_numpy(prob["q"])                          # [qo, hq, d]
+        rep = hq // hkv
+        k = k.repeat_interleave(rep, dim=1).permute(1, 0, 2)     # [hq, kv, d]
+        v = v.repeat_interleave(rep, dim=1).permute(1, 0, 2)
+        qh = q.permute(1, 0, 2)
+        keep = torch.ones(qo, kv, dtype=torch.bool)
+        if causal:   # bottom-right: j - i <= kv - qo
+            keep = torch.tril(keep, diagonal=kv - qo)
+        if w != -1:  # left band: j - i >= kv - qo - w
+            keep = keep & torch.triu(torch.ones(qo, kv, dtype=torch.bool), diagonal=kv - qo - w)
+        if causal and w == -1 and qo == kv:
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qh, k, v, is_causal=True, scale=0.25)
+        else:
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qh, k, v, attn_mask=keep, scale=0.25)
+        scores = (qh @ k.transpose(1, 2)) * 0.25
+        ref_lse = torch.logsumexp(scores.masked_fill(~keep, float("-inf")), dim=-1)
+        np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), atol=1e-10)
+        np.testing.assert_allclose(lse, ref_lse.permute(1, 0).numpy(), atol=1e-10)
+
+
+def check_bruteforce_grid(attn_fn, rng, brute_fn=oracle.attention_bruteforce, quick=False):
+    heads = [(1, 1), (4, 2), (6, 3)]
+    pages = [1, 3, 16]
+    n = 0
+    for hq, hkv in heads:
+        for P in pages:
+            B = int(rng.integers(1, 4))
+            qo = rng.integers(1, 9, size=B)
+            kv = np.maximum(qo, rng.integers(1, 41, size=B))
+            prob = small_problem(rng, qo, kv, hq, hkv, 3, P)
+            L = int(kv.max())
+            for causal in (True, False):
+                for w in sorted({-1, 0, 1, max(L - 2, 0), L - 1, L, L + 5}):
+                    if quick and n % 5:
+                        n += 1
+                        continue
+                    a = attn_fn(**prob, causal=causal, window_left=w, sm_scale=0.7)
+                    bf = brute_fn(**prob, causal=causal, window_left=w, sm_scale=0.7)
+                    np.testing.assert_allclose(a[0], bf[0], atol=1e-9)
+                    np.testing.assert_allclose(a[1], bf[1], atol=1e-9)
+                    n += 1
+    return n
+
+
+# ---------------------------------------------------------------------------
+# the tests
+# ---------------------------------------------------------------------------
+
+def test_golden_mask_ranges():
+    check_golden_masks(oracle.allowed_mask)
+
+
+def test_golden_tiny_attention():
+    check_golden_attention(oracle.attention)
+    check_golden_attention(oracle.attention_bruteforce)
+
+
+def test_kv_lengths_from_paged_metadata():
+    check_kv_lengths(oracle.kv_lengths)
+
+
+def test_gather_follows_page_table():
+    check_gather(oracle.gather_request_kv)
+
+
+def test_bruteforce_matches_vectorised_on_grid():
+    assert check_bruteforce_grid(oracle.attention, np.random.default_rng(11)) > 100
+
+
+def test_closed_form_zero_keys():
+    check_closed_form_k_zero(oracle.attention, np.random.default_rng(12))
+
+
+def test_rows_sum_to_one():
+    check_v_ones(oracle.attention, np.random.default_rng(13))
+
+
+def test_library_sdpa_special_cases():
+    check_sdpa(oracle.attention, np.random.default_rng(14))
+
+
+def test_wide_window_equals_no_window():
+    rng = np.random.default_rng(15)
+    prob = small_problem(rng, [4, 9], [20, 20], 4, 2, 8, 16)
+    base = oracle.attention(**prob, causal=True, window_left=-1, sm_scale=0.3)
+    for w in (19, 20, 500):
+        got = oracle.attention(**prob, causal=True, window_left=w, sm_scale=0.3)
+        np.testing.assert_array_equal(got[0], base[0])
+        np.testing.assert_array_equal(got[1], base[1])
+    narrower = oracle.attention(**prob, causal=True, window_left=18, sm_scale=0.3)
+    assert np.abs(narrower[0] - base[0]).max() > 1e-3
+
+
+def test_gqa_equals_replicated_kv_heads():
+    rng = np.random.default_rng(16)
+    prob = small_problem(rng, [5, 3], [12, 30], 6, 2, 8, 4)
+    got = oracle.attention(**prob, causal=True, window_left=7, sm_scale=0.4)
+    rep = dict(prob)
+    rep["k_pool"] = np.repeat(prob["k_pool"], 3, axis=2)
+    rep["v_pool"] = np.repeat(prob["v_pool"], 3, axis=2)
+    rep["num_kv_heads"] = 6
+    want = oracle.attention(**rep, causal=True, window_left=7, sm_scale=0.4)
+    np.testing.assert_allclose(got[0], want[0], atol=1e-14)
+    np.testing.assert_allclose(got[1], want[1], atol=1e-14)
+
+
+def test_page_relabelling_is_invisible():
+    rng = np.random.default_rng(17)
+    prob = small_problem(rng, [5, 7], [33, 18], 4, 4, 8, 4)
+    got = oracle.attention(**prob, causal=True, window_left=-1, sm_scale=0.4)
+    perm = rng.permutation(prob["k_pool"].shape[0])
+    moved = dict(prob)
+    moved["k_pool"] = np.empty_like(prob["k_pool"])
+    moved["v_pool"] = np.empty_like(prob["v_pool"])
+    moved["k_pool"][perm] = prob["k_pool"]
+    moved["v_pool"][perm] = prob["v_pool"]
+    moved["kv_page_indices"] = perm[prob["kv_page_indices"]]
+    want = oracle.attention(**moved, causal=True, window_left=-1, sm_scale=0.4)
+    np.testing.assert_array_equal(got[0], want[0])
+    np.testing.assert_array_equal(got[1], want[1])
+
+
+def test_last_verify_row_equals_decode():
+    rng = np.random.default_rng(18)
+    prob = small_problem(rng, [4, 4, 4], [9, 40, 17], 8, 2, 8, 16)
+    o, lse = oracle.attention(**prob, causal=True, window_left=-1, sm_scale=0.5)
+    dec = dict(prob)
+    dec["q"] = prob["q"][[3, 7, 11]]
+    dec["qo_indptr"] = np.arange(4)
+    od, lsed = oracle.attention(**dec, causal=True, window_left=-1, sm_scale=0.5)
+    np.testing.assert_allclose(o[[3, 7, 11]], od, atol=1e-14)
+    np.testing.assert_allclose(lse[[3, 7, 11]], lsed, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,w", [(True, -1), (True, 13), (False, 5), (False, -1)])
+def test_split_then_merge_equals_unsplit(causal, w):
+    rng = np.random.default_rng(19)
+    prob = small_problem(rng, [6, 1, 9], [50, 37, 64], 4, 2, 8, 16)
+    whole = oracle.attention(**prob, causal=causal, window_left=w, sm_scale=0.4)
+    bounds = [0, 7, 16, 16, 40, 64]
+    parts = [oracle.attention(**prob, causal=causal, window_left=w, sm_scale=0.4,
+                              kv_begin=a, kv_end=e) for a, e in zip(bounds[:-1], bounds[1:])]
+    o, lse = oracle.merge_many([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(o, whole[0], atol=1e-12)
+    np.testing.assert_allclose(lse, whole[1], atol=1e-12)
+    # an empty chunk is (0, -inf)
+    empty = parts[2]
+    assert np.all(np.isneginf(empty[1])) and np.all(empty[0] == 0)
+
+
+def test_merge_algebra():
+    rng = np.random.default_rng(20)
+    o = [rng.standard_normal((5, 3, 4)) for _ in range(3)]
+    lse = [rng.standard_normal((5, 3)) * 4 for _ in range(3)]
+    ab = oracle.merge_states(o[0], lse[0], o[1], lse[1])
+    ba = oracle.merge_states(o[1], lse[1], o[0], lse[0])
+    np.testing.assert_allclose(ab[0], ba[0], atol=1e-14)
+    np.testing.assert_allclose(ab[1], ba[1], atol=1e-14)
+    left = oracle.merge_states(*ab, o[2], lse[2])
+    bc = oracle.merge_states(o[1], lse[1], o[2], lse[2])
+    right = oracle.merge_states(o[0], lse[0], *bc)
+    np.testing.assert_allclose(left[0], right[0], atol=1e-12)
+    np.testing.assert_allclose(left[1], right[1], atol=1e-12)
+    # closed form: two equal states merge to themselves with lse + log 2
+    same = oracle.merge_states(o[0], lse[0], o[0], lse[0])
+    np.testing.assert_allclose(same[0], o[0], atol=1e-14)
+    np.testing.assert_allclose(same[1], lse[0] + math.log(2), atol=1e-14)
+    # -inf is the identity, exactly; two -inf give (0, -inf)
+    ninf = np.full((5, 3), -np.inf)
+    idn = oracle.merge_states(o[0], lse[0], np.zeros_like(o[0]), ninf)
+    np.testing.assert_array_equal(idn[0], o[0])
+    np.testing.assert_array_equal(idn[1], lse[0])
+    both = oracle.merge_states(o[0], ninf, o[1], ninf)
+    assert np.all(both[0] == 0) and np.all(np.isneginf(both[1]))
+
+
+def test_non_vacuity_on_workloads():
+    """Windowed vs unwindowed, causal vs not, and a wrong GQA map all differ by > 0.1."""
+    w = workloads.config1(window_left=31)
+    q, k, v = w.float_inputs()
+    args = w.plan_args()
+    del args["head_dim"]
+    base = oracle.attention(q, k, v, **{**args, "window_left": -1})
+    win = oracle.attention(q, k, v, **args)
+    nonc = oracle.attention(q, k, v, **{**args, "window_left": -1, "causal": False})
+    assert np.abs(base[0] - win[0]).max() > 0.1
+    assert np.abs(base[0] - nonc[0]).max() > 0.1
+    # wrong GQA mapping: interleaved (h % Hkv) instead of consecutive groups
+    k_swapped = k[:, :, ::-1, :].copy()
+    v_swapped = v[:, :, ::-1, :].copy()
+    wrong = oracle.attention(q, k_swapped, v_swapped, **{**args, "window_left": -1})
+    assert np.abs(base[0] - wrong[0]).max() > 0.1
+
+
+def test_refuses_indivisible_heads():
+    rng = np.random.default_rng(21)
+    prob = small_problem(rng, [2], [4], 4, 4, 4, 2)
+    prob["num_qo_heads"], prob["num_kv_heads"] = 12, 8
+    with pytest.raises(ValueError):
+        oracle.attention(**prob, causal=True, window_left=-1, sm_scale=1.0)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: every pin family must reject a plausible wrong oracle
+# ---------------------------------------------------------------------------
+
+def _top_left_causal(qo_len, kv_len, causal, window_left, kv_begin=None, kv_end=None):
+    m = oracle.allowed_mask(qo_len, kv_len, False, window_left, kv_begin, kv_end)
+    if causal:
+        i = np.arange(qo_len)[:, None]
+        j = np.arange(kv_len)[None, :]
+        m &= j <= i
+    return m
+
+
+def _window_off_by_one(qo_len, kv_len, causal, window_left, kv_begin=None, kv_end=None):
+    w = window_left if window_left == -1 else window_left + 1
+    return oracle.allowed_mask(qo_len, kv_len, causal, w, kv_begin, kv_end)
+
+
+def _with_mask(mask_fn):
+    def attn(*a, **kw):
+        saved = oracle.attention.__globals__["allowed_mask"]
+        oracle.attention.__globals__["allowed_mask"] = mask_fn
+        try:
+            return oracle.attention(*a, **kw)
+        finally:
+            oracle.attention.__globals__["allowed_mask"] = saved
+    return attn
+
+
+def _scale_dropped(*a, **kw):
+    a = list(a)
+    if "sm_scale" in kw:
+        kw["sm_scale"] = 1.0
+    elif len(a) > 12:
+        a[12] = 1.0
+    return oracle.attention(*a, **kw)
+
+
+def _log2_lse(*a, **kw):
+    o, lse = oracle.attention(*a, **kw)
+    return o, lse / math.log(2)
+
+
+def _interleaved_gqa(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
+                     kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
+                     window_left, sm_scale, **kw):
+    # q head h reads kv head h % Hkv instead of h // group
+    group = num_qo_heads // num_kv_heads
+    order = [(h % num_kv_heads) * group + h // num_kv_heads for h in range(num_qo_heads)]
+    inv = np.argsort(order)
+    o, lse = oracle.attention(np.asarray(q)[:, order], k_pool, v_pool, qo_indptr,
+                              kv_indptr, kv_page_indices, kv_last_page_len,
+                              num_qo_heads, num_kv_heads, page_size, causal,
+                              window_left, sm_scale, **kw)
+    return o[:, inv], lse[:, inv]
+
+
+def _slot_from_wrong_page(pool, kv_indptr, kv_page_indices, b, kv_len, page_size):
+    # uses the logical page number instead of the page table
+    rows = [pool[j // page_size, j % page_size] for j in range(int(kv_len))]
+    return np.stack(rows).astype(np.float64) if rows else np.zeros((0,) + pool.shape[2:])
+
+
+def _transposed_pv(*a, **kw):
+    o, lse = oracle.attention(*a, **kw)
+    return o[..., ::-1], lse
+
+
+@pytest.mark.parametrize("name", ["top_left_causal", "window_off_by_one", "scale_dropped",
+                                  "log2_lse", "interleaved_gqa", "wrong_page",
+                                  "reversed_head_dim"])
+def test_pins_reject_planted_mistakes(name):
+    rng = np.random.default_rng(22)
+
+    def fails(check, *args):
+        try:
+            check(*args)
+        except AssertionError:
+            return True
+        return False
+
+    if name == "top_left_causal":
+        assert fails(check_golden_masks, _top_left_causal)
+        assert fails(check_sdpa, _with_mask(_top_left_causal), rng)
+    elif name == "window_off_by_one":
+        assert fails(check_golden_masks, _window_off_by_one)
+        assert fails(check_closed_form_k_zero, _with_mask(_window_off_by_one), rng)
+    elif name == "scale_dropped":
+        assert fails(check_golden_attention, _scale_dropped)
+        assert fails(check_sdpa, _scale_dropped, rng)
+    elif name == "log2_lse":
+        assert fails(check_golden_attention, _log2_lse)
+        assert fails(check_closed_form_k_zero, _log2_lse, rng)
+    elif name == "interleaved_gqa":
+        assert fails(check_golden_attention, _interleaved_gqa) or \
+            fails(check_sdpa, _interleaved_gqa, rng)
+        assert fails(check_sdpa, _interleaved_gqa, rng)
+    elif name == "wrong_page":
+        assert fails(check_gather, _slot_from_wrong_page)
+    elif name == "reversed_head_dim":
+        assert fails(check_golden_attention, _transposed_pv)
+        assert fails(check_sdpa, _transposed_pv, rng)
