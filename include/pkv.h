@@ -1,0 +1,222 @@
+/*
+ * pkv.h -- C ABI of a paged-KV attention prefill library for AMD MI355X (gfx950).
+ *
+ * The library computes, for a batch of requests whose keys and values live in
+ * a paged KV cache, masked softmax(sm_scale * Q K^T) V with grouped-query
+ * heads, plus the per-row log-sum-exp, and merges partial (o, lse) states.
+ *
+ * Sources (web pages of the AMD-Ecosystem FlashInfer fork):
+ *   PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
+ *     section "Why window_size_right stays -1": the sliding window keeps key j
+ *     for query row i only when j + qo_len + window_left >= kv_len + i; it is
+ *     left-only, anchored bottom-right and applied independently of causal;
+ *     window_left = -1 means no window.  Section "What changed": a window at
+ *     least as wide as the sequence is normalised to -1, with a signed compare.
+ *   PR #362 "Support speculative-decode verify on ROCm, and stop auto routing
+ *     short-query prefill to AITER", Summary: the causal mask is bottom-right
+ *     aligned (the last query row sees every key), which is exactly chain
+ *     speculative-verify semantics: verify is a causal prefill whose
+ *     qo_indptr advances by the draft length.  Review notes: kv_len comes from
+ *     the paged metadata (indptr and last_page_len), and kv_len < qo_len under
+ *     the causal mask gives a silently wrong answer.
+ *   PR #399 "Refuse attention inputs the ROCm kernels would compute wrongly",
+ *     What changed: strided last dimensions, run() tensors that disagree with
+ *     plan() (token counts are minimums), and head counts the GQA group cannot
+ *     divide (or zero kv heads) are refused; a rejected plan leaves the
+ *     previous one usable; partial (o, lse) states are merged in place.
+ *
+ * Conventions for every entry point:
+ *   - Host arrays are read during the call only; nothing keeps a view of them.
+ *   - Device pointers are caller-owned (allocated by PyTorch or hipMalloc).
+ *   - `stream` is a hipStream_t (NULL = the default stream); all device work is
+ *     stream-ordered on it and no call synchronises the host with the device.
+ *   - Strides are in elements; the last (head_dim) dimension is always packed.
+ *     Device base pointers must be 16-byte aligned and token / head / page
+ *     strides multiples of 8 elements (16-byte vector loads).
+ *   - A refused call returns a non-zero status before any device write or
+ *     kernel launch; pkv_last_error() then names the field, the expected value
+ *     and the given value.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,      /* argument out of range (lengths, window, page ids, dtype, ...) */
+  PKV_ELAYOUT = 2,     /* stride / alignment / packing not supported */
+  PKV_EGQA = 3,        /* num_qo_heads not a positive multiple of num_kv_heads */
+  PKV_EMISMATCH = 4,   /* run() tensors disagree with the plan */
+  PKV_ENOTPLANNED = 5, /* plan handle missing or built without a workspace */
+  PKV_EHIP = 6,        /* a HIP runtime call failed */
+  PKV_EWORKSPACE = 7   /* workspace missing or too small */
+} pkv_status;
+
+typedef enum { PKV_FP16 = 0, PKV_BF16 = 1, PKV_FP32 = 2 } pkv_dtype;
+
+typedef struct pkv_plan_s* pkv_plan_t;
+
+/* Optional plan knobs (pass NULL for the defaults). */
+typedef struct {
+  /* 0: the scheduler chooses how many KV chunks each query tile is split into.
+     >0: split every request's keys [0, kv_len) into this many equal chunks in
+     the request's own key coordinates (sizes rounded up to the key tile), each
+     chunk producing a partial (o, lse) that run() merges. */
+  int32_t num_kv_chunks;
+  /* Restrict every request to keys in [kv_begin, kv_end) of its own key
+     coordinates (kv_end < 0: no upper limit).  The mask is still evaluated in
+     those coordinates, so the result is the partial state of that key range:
+     rows that see no key there get o = 0 and lse = -inf. */
+  int32_t kv_begin;
+  int32_t kv_end;
+  /* 0: automatic; 1: prefill tile (128 packed rows x 64 keys);
+     2: short-query tile (16 or 32 packed rows x 128 keys). */
+  int32_t tile;
+  int32_t reserved[4];
+} pkv_plan_options;
+
+/* Scheduling summary of a plan. */
+typedef struct {
+  int64_t total_q_rows;      /* qo_indptr[batch] */
+  int64_t num_page_indices;  /* kv_indptr[batch] */
+  int32_t batch_size;
+  int32_t num_work_items;    /* attention work-group tasks */
+  int32_t num_merge_items;   /* query tiles whose KV was split */
+  int32_t num_partial_slots; /* fp32 partial states in the float workspace */
+  int32_t tile_rows;         /* packed (position, head) rows per task */
+  int32_t tile_keys;         /* keys per inner iteration */
+  int32_t max_page_index;    /* largest page id referenced (-1 if none) */
+  int32_t has_device_copy;   /* 1 when built with a workspace (runnable) */
+  int64_t int_ws_bytes;
+  int64_t float_ws_bytes;
+} pkv_plan_info;
+
+/*
+ * Workspace sizes for a plan with these arguments (host-only; no device call).
+ * Arguments are those of pkv_plan.  Fails with the same refusals as pkv_plan.
+ */
+pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                              const int32_t* kv_page_indices,
+                              const int32_t* kv_last_page_len, int32_t batch_size,
+                              int32_t num_qo_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t causal,
+                              int32_t window_left, const pkv_plan_options* opts,
+                              size_t* int_ws_bytes, size_t* float_ws_bytes);
+
+/*
+ * plan: validate the batch and schedule it.
+ *   qo_indptr[batch+1]   host; request b owns query rows [qo_indptr[b], qo_indptr[b+1]).
+ *   kv_indptr[batch+1]   host; request b owns page-table entries [kv_indptr[b], kv_indptr[b+1]).
+ *   kv_page_indices[kv_indptr[batch]]  host; physical page ids.
+ *   kv_last_page_len[batch]  host; keys on the request's last page, in [1, page_size]
+ *                        when it has a page.  kv_len = (pages - 1) * page_size + last.
+ *   num_qo_heads / num_kv_heads: q head h reads kv head h / (num_qo_heads / num_kv_heads).
+ *   head_dim in {64, 128}; page_size >= 1; causal 0/1 (bottom-right aligned);
+ *   window_left >= -1 (-1 = no window); sm_scale finite; dtype PKV_FP16 or PKV_BF16.
+ *   int_ws / float_ws: device workspaces of at least the sizes pkv_workspace_size
+ *   reports.  The plan writes its task list into int_ws (one async copy on
+ *   `stream`) and run() keeps fp32 partial states in float_ws: both must stay
+ *   allocated and otherwise untouched while the plan is in use.  int_ws = NULL
+ *   with int_ws_bytes = 0 builds a host-only plan (inspectable, not runnable).
+ * Refused (no handle is returned, earlier plans stay valid): decreasing indptr,
+ *   indptr[0] != 0, last_page_len out of range, negative page ids, head counts
+ *   GQA cannot divide, head_dim not 64/128, window_left < -1, a causal request
+ *   with kv_len < qo_len, a request with query rows and no key, a too-small
+ *   workspace.
+ * On success *out_plan owns a copy of everything it needs; free it with
+ * pkv_plan_destroy.
+ */
+pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                    int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t causal,
+                    int32_t window_left, float sm_scale, pkv_dtype dtype,
+                    void* int_ws, size_t int_ws_bytes, void* float_ws,
+                    size_t float_ws_bytes, void* stream,
+                    const pkv_plan_options* opts, pkv_plan_t* out_plan);
+
+/*
+ * run: attention over the planned batch.
+ *   q  [q_rows, q_heads, q_dim] at q + row*q_s_tok + head*q_s_head (+ d).
+ *   k, v: paged pools, logical order [pages, page_size, heads, head_dim] at
+ *     base + page*s_page + slot*s_tok + head*s_head (+ d): NHD, HND and
+ *     combined K/V caches are all views of this with the right strides.
+ *   o  [o_rows, num_qo_heads, head_dim] packed, in dtype; row r of request b is
+ *     o[qo_indptr[b] + r].
+ *   lse [o_rows, num_qo_heads] packed fp32, natural log; NULL to skip.
+ * Shapes are checked against the plan: heads, head_dim (q, k, v separately),
+ * page_size and dtype must match; q_rows and o_rows are minimums (callers pad);
+ * every referenced page id must be below k_pages and v_pages.
+ */
+pkv_status pkv_run(pkv_plan_t plan,
+                   const void* q, int64_t q_rows, int32_t q_heads, int32_t q_dim,
+                   int64_t q_s_tok, int64_t q_s_head,
+                   const void* k, int64_t k_pages, int32_t k_page_size, int32_t k_heads,
+                   int32_t k_dim, int64_t k_s_page, int64_t k_s_tok, int64_t k_s_head,
+                   const void* v, int64_t v_pages, int32_t v_page_size, int32_t v_heads,
+                   int32_t v_dim, int64_t v_s_page, int64_t v_s_tok, int64_t v_s_head,
+                   pkv_dtype dtype, void* o, int64_t o_rows, float* lse, void* stream);
+
+/*
+ * merge_states: combine two partial attention states over disjoint key sets
+ * (PR #399, What changed / graph-mode partial_state merge; PR #362's split-KV
+ * tests).  With M = max(lse_a, lse_b), w_x = exp(lse_x - M):
+ *   o = (w_a o_a + w_b o_b) / (w_a + w_b),  lse = M + log(w_a + w_b);
+ * two -inf inputs give (0, -inf), and a -inf side leaves the other unchanged.
+ *   o_a, o_b, o_out: [rows, heads, head_dim] packed, dtype PKV_FP16/BF16/FP32.
+ *   lse_a, lse_b, lse_out: [rows, heads] packed fp32 (natural log).
+ * o_out / lse_out may alias o_a / lse_a (in-place merge).  Device pointers.
+ */
+pkv_status pkv_merge_states(const void* o_a, const float* lse_a, const void* o_b,
+                            const float* lse_b, void* o_out, float* lse_out,
+                            int64_t rows, int32_t heads, int32_t head_dim,
+                            pkv_dtype dtype, void* stream);
+
+/*
+ * debug_gather: write the logical K and V rows of every planned request,
+ * [sum kv_len, kv_heads, head_dim] in request order, through the same page
+ * address path the attention kernel reads (for bit-exact gather checks).
+ * Arguments as in pkv_run; k_out / v_out are packed device buffers.
+ */
+pkv_status pkv_debug_gather(pkv_plan_t plan,
+                            const void* k, int64_t k_pages, int32_t k_page_size,
+                            int32_t k_heads, int32_t k_dim, int64_t k_s_page,
+                            int64_t k_s_tok, int64_t k_s_head,
+                            const void* v, int64_t v_pages, int32_t v_page_size,
+                            int32_t v_heads, int32_t v_dim, int64_t v_s_page,
+                            int64_t v_s_tok, int64_t v_s_head, pkv_dtype dtype,
+                            void* k_out, void* v_out, int64_t out_rows, void* stream);
+
+/* Scheduling summary of a plan (host-only). */
+pkv_status pkv_plan_get_info(pkv_plan_t plan, pkv_plan_info* info);
+
+/*
+ * Copy the plan's task list to host memory as int32 records of 8 fields:
+ * {request, kv_head, row0, num_rows, kv_begin, kv_end, partial_slot, 0}
+ * (rows are packed (position, head-in-group) rows of that kv head; a
+ * partial_slot >= 0 marks one chunk of a split query tile).  Writes at most
+ * `capacity` records and stores the total count in *count.  Host-only.
+ */
+pkv_status pkv_plan_get_work(pkv_plan_t plan, int32_t* out, int64_t capacity,
+                             int64_t* count);
+
+/* Release a plan (never touches the workspaces).  NULL is a no-op. */
+void pkv_plan_destroy(pkv_plan_t plan);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -247,3 +247,41 @@ def merge_many(os, lses):
     for o_c, lse_c in zip(os[1:], lses[1:]):
         o, lse = merge_states(o, lse, o_c, lse_c)
     return np.asarray(o, dtype=np.float64), np.asarray(lse, dtype=np.float64)
+
+
+def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
+                   kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
+                   window_left, sm_scale, b, rows, heads, kv_begin=None, kv_end=None):
+    """``attention`` restricted to some rows and q heads of request b.
+
+    Same definition, float64; used to check full-size workloads on sampled
+    outputs.  rows are request-local query indices, heads q-head indices.
+    Returns o [len(rows), len(heads), D] and lse [len(rows), len(heads)].
+    The request's keys are read page by page through its page table.
+    """
+    _check_heads(num_qo_heads, num_kv_heads)
+    group = num_qo_heads // num_kv_heads
+    L = int(kv_lengths(kv_indptr, kv_last_page_len, page_size)[b])
+    q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+    qo_len = q1 - q0
+    first, n_pages = int(kv_indptr[b]), int(kv_indptr[b + 1]) - int(kv_indptr[b])
+    pages = np.asarray(kv_page_indices[first:first + n_pages], dtype=np.int64)
+    mask = allowed_mask(qo_len, L, causal, window_left, kv_begin, kv_end)
+    d = np.shape(q)[2]
+    o = np.zeros((len(rows), len(heads), d), dtype=np.float64)
+    lse = np.full((len(rows), len(heads)), NEG_INF, dtype=np.float64)
+    for hi_, h in enumerate(heads):
+        g = h // group
+        kb = np.asarray(k_pool[pages, :, g, :], dtype=np.float64).reshape(-1, d)[:L]
+        vb = np.asarray(v_pool[pages, :, g, :], dtype=np.float64).reshape(-1, d)[:L]
+        for ri, i in enumerate(rows):
+            ok = mask[i]
+            if not ok.any():
+                continue
+            s = sm_scale * (kb[ok] @ np.asarray(q[q0 + i, h, :], dtype=np.float64))
+            m = s.max()
+            e = np.exp(s - m)
+            total = e.sum()
+            lse[ri, hi_] = m + np.log(total)
+            o[ri, hi_] = (e / total) @ vb[ok]
+    return o, lse

@@ -1,0 +1,420 @@
+"""Paged-KV attention prefill for AMD MI355X (gfx950): thin Python binding.
+
+    p = plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len,
+             num_qo_heads, num_kv_heads, head_dim, page_size, causal,
+             window_left=-1, sm_scale=None, dtype=torch.bfloat16)
+    o, lse = p.run(q, paged_k, paged_v)
+    o, lse = merge_states(o_a, lse_a, o_b, lse_b)
+
+Every step of the computation runs in the HIP library ``libpkv.so`` (C ABI in
+include/pkv.h); this module only marshals arguments.  PyTorch supplies device
+memory and the current stream.  There is no fallback: without the built
+library, or on a machine without a GPU, calls that compute raise.
+
+Semantics (AMD-Ecosystem FlashInfer fork, PR #339 section "Why
+window_size_right stays -1"; PR #362 Summary; PR #399 What changed): masked
+softmax(sm_scale * Q K^T) V with a bottom-right causal mask, an optional
+left-only window (key j kept for row i when j + qo_len + window_left >=
+kv_len + i), GQA (q head h reads kv head h // (Hq // Hkv)), natural-log lse.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+__all__ = ["plan", "plan_host", "verify_plan", "workspace_size", "merge_states", "Plan",
+           "PkvError", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+_lib = None
+
+PKV_OK, PKV_EINVAL, PKV_ELAYOUT, PKV_EGQA, PKV_EMISMATCH, PKV_ENOTPLANNED, PKV_EHIP, \
+    PKV_EWORKSPACE = range(8)
+_STATUS_NAMES = ["OK", "EINVAL", "ELAYOUT", "EGQA", "EMISMATCH", "ENOTPLANNED", "EHIP",
+                 "EWORKSPACE"]
+PKV_FP16, PKV_BF16, PKV_FP32 = 0, 1, 2
+
+
+class PkvError(ValueError):
+    """A call refused by the library (status and message from pkv_last_error)."""
+
+    def __init__(self, status, message):
+        self.status = status
+        self.status_name = _STATUS_NAMES[status] if 0 <= status < len(_STATUS_NAMES) else str(status)
+        super().__init__(f"[{self.status_name}] {message}")
+
+
+class _PlanOptions(ctypes.Structure):
+    _fields_ = [("num_kv_chunks", ctypes.c_int32), ("kv_begin", ctypes.c_int32),
+                ("kv_end", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("total_q_rows", ctypes.c_int64), ("num_page_indices", ctypes.c_int64),
+                ("batch_size", ctypes.c_int32), ("num_work_items", ctypes.c_int32),
+                ("num_merge_items", ctypes.c_int32), ("num_partial_slots", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("tile_keys", ctypes.c_int32),
+                ("max_page_index", ctypes.c_int32), ("has_device_copy", ctypes.c_int32),
+                ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64)]
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpkv.so (built in-tree by paged_kv_cache_prefill_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_cache_prefill_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_version.restype = ctypes.c_char_p
+    lib.pkv_workspace_size.argtypes = [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.POINTER(_PlanOptions), ctypes.POINTER(sz),
+                                       ctypes.POINTER(sz)]
+    lib.pkv_plan.argtypes = [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32, i32, i32,
+                             ctypes.c_float, ctypes.c_int, vp, sz, vp, sz, vp,
+                             ctypes.POINTER(_PlanOptions), ctypes.POINTER(vp)]
+    lib.pkv_run.argtypes = [vp, vp, i64, i32, i32, i64, i64,
+                            vp, i64, i32, i32, i32, i64, i64, i64,
+                            vp, i64, i32, i32, i32, i64, i64, i64,
+                            ctypes.c_int, vp, i64, vp, vp]
+    lib.pkv_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
+    lib.pkv_debug_gather.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, i64,
+                                     vp, i64, i32, i32, i32, i64, i64, i64,
+                                     ctypes.c_int, vp, vp, i64, vp]
+    lib.pkv_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
+    lib.pkv_plan_get_work.argtypes = [vp, pi32, i64, ctypes.POINTER(i64)]
+    lib.pkv_plan_destroy.argtypes = [vp]
+    lib.pkv_plan_destroy.restype = None
+    for name in ("pkv_workspace_size", "pkv_plan", "pkv_run", "pkv_merge_states",
+                 "pkv_debug_gather", "pkv_plan_get_info", "pkv_plan_get_work"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != PKV_OK:
+        msg = _lib.pkv_last_error().decode(errors="replace")
+        if status == PKV_EHIP:
+            raise RuntimeError(f"[EHIP] {msg}")
+        raise PkvError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dtype):
+    torch = _torch()
+    if dtype in (torch.bfloat16, "bf16", "bfloat16"):
+        return PKV_BF16
+    if dtype in (torch.float16, "fp16", "float16"):
+        return PKV_FP16
+    if dtype in (torch.float32, "fp32", "float32"):
+        return PKV_FP32
+    raise PkvError(PKV_EINVAL, f"dtype: expected fp16 or bf16, given {dtype}")
+
+
+def _host_i32(x, name):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        if x.is_cuda:
+            raise PkvError(PKV_EINVAL, f"{name}: expected a host array, given a device tensor")
+        x = x.detach().numpy()
+    a = np.ascontiguousarray(np.asarray(x), dtype=np.int64)
+    if a.ndim != 1:
+        raise PkvError(PKV_EINVAL, f"{name}: expected a 1-D array, given shape {a.shape}")
+    if a.size and (a.min() < -(2 ** 31) or a.max() >= 2 ** 31):
+        raise PkvError(PKV_EINVAL, f"{name}: values must fit in int32")
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr_i32(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if a is not None and a.size else None
+
+
+def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0):
+    o = _PlanOptions()
+    o.num_kv_chunks, o.kv_begin, o.kv_end, o.tile = int(num_kv_chunks), int(kv_begin), \
+        int(kv_end), int(tile)
+    return o
+
+
+def _plan_arrays(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len):
+    qo = _host_i32(qo_indptr, "qo_indptr")
+    kv = _host_i32(kv_indptr, "kv_indptr")
+    idx = _host_i32(kv_page_indices, "kv_page_indices")
+    last = _host_i32(kv_last_page_len, "kv_last_page_len")
+    batch = len(qo) - 1
+    if batch < 0 or len(kv) != batch + 1 or len(last) != batch:
+        raise PkvError(PKV_EINVAL, f"qo_indptr / kv_indptr / kv_last_page_len: expected lengths "
+                                   f"B+1, B+1, B; given {len(qo)}, {len(kv)}, {len(last)}")
+    n = int(kv[-1]) if batch > 0 else 0
+    if idx is None or len(idx) < n:
+        raise PkvError(PKV_EINVAL, f"kv_page_indices: expected {n} entries (kv_indptr[-1]), "
+                                   f"given {0 if idx is None else len(idx)}")
+    return qo, kv, idx, last, batch
+
+
+def workspace_size(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
+                   num_kv_heads, head_dim, page_size, causal, window_left=-1, **opts):
+    """(int workspace bytes, float workspace bytes) a plan with these arguments needs."""
+    lib = load_library()
+    qo, kv, idx, last, batch = _plan_arrays(qo_indptr, kv_indptr, kv_page_indices,
+                                            kv_last_page_len)
+    ib, fb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    o = _options(**opts)
+    _check(lib.pkv_workspace_size(_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), _ptr_i32(last),
+                                  batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                  int(bool(causal)), int(window_left), ctypes.byref(o),
+                                  ctypes.byref(ib), ctypes.byref(fb)))
+    return ib.value, fb.value
+
+
+class Plan:
+    """A validated, scheduled batch.  Owns its device workspaces."""
+
+    def __init__(self, handle, dtype, head_dim, num_qo_heads, num_kv_heads, page_size, device,
+                 int_ws, float_ws):
+        self._h = ctypes.c_void_p(handle)
+        self.dtype = dtype
+        self.head_dim = head_dim
+        self.num_qo_heads = num_qo_heads
+        self.num_kv_heads = num_kv_heads
+        self.page_size = page_size
+        self.device = device
+        self._int_ws = int_ws
+        self._float_ws = float_ws
+        info = _PlanInfo()
+        _check(_lib.pkv_plan_get_info(self._h, ctypes.byref(info)))
+        self.info = {name: getattr(info, name) for name, _ in _PlanInfo._fields_}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pkv_plan_destroy(h)
+            self._h = None
+
+    @property
+    def total_q_rows(self):
+        return self.info["total_q_rows"]
+
+    def work_items(self):
+        """Task list as an int32 array [n, 8]:
+        (request, kv_head, row0, num_rows, kv_begin, kv_end, partial_slot, tile_begin)."""
+        n = ctypes.c_int64(0)
+        _check(_lib.pkv_plan_get_work(self._h, None, 0, ctypes.byref(n)))
+        out = np.zeros((n.value, 8), dtype=np.int32)
+        if n.value:
+            _check(_lib.pkv_plan_get_work(self._h, _ptr_i32(out.reshape(-1)), n.value,
+                                          ctypes.byref(n)))
+        return out
+
+    @staticmethod
+    def _cache_view(x, kv_layout):
+        if x.dim() != 4:
+            raise PkvError(PKV_ELAYOUT, f"paged cache: expected 4-D, given {x.dim()}-D")
+        if kv_layout == "HND":      # [pages, heads, page_size, dim] -> logical NHD
+            x = x.permute(0, 2, 1, 3)
+        elif kv_layout != "NHD":
+            raise PkvError(PKV_EINVAL, f"kv_layout: expected 'NHD' or 'HND', given {kv_layout!r}")
+        if x.stride(3) != 1:
+            raise PkvError(PKV_ELAYOUT, f"paged cache: head_dim stride must be 1, given "
+                                        f"{x.stride(3)}")
+        return x
+
+    def _stream(self, stream):
+        torch = _torch()
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        return ctypes.c_void_p(stream.cuda_stream)
+
+    def run(self, q, paged_k, paged_v, out=None, lse=None, return_lse=True, kv_layout="NHD",
+            stream=None):
+        """Attention over the planned batch -> (o, lse or None)."""
+        torch = _torch()
+        if self._int_ws is None:
+            raise PkvError(PKV_ENOTPLANNED, "plan was built host-only; it cannot run")
+        if q.dim() != 3:
+            raise PkvError(PKV_ELAYOUT, f"q: expected [rows, heads, head_dim], given {q.dim()}-D")
+        if q.stride(2) != 1:
+            raise PkvError(PKV_ELAYOUT, f"q: head_dim stride must be 1, given {q.stride(2)}")
+        for name, t in (("q", q), ("paged_k", paged_k), ("paged_v", paged_v)):
+            if t.dtype != self.dtype:
+                raise PkvError(PKV_EMISMATCH, f"{name} dtype: planned {self.dtype}, given {t.dtype}")
+            if t.device != self.device:
+                raise PkvError(PKV_EMISMATCH, f"{name} device: planned {self.device}, given {t.device}")
+        k = self._cache_view(paged_k, kv_layout)
+        v = self._cache_view(paged_v, kv_layout)
+        rows = self.total_q_rows
+        if out is None:
+            out = torch.empty((rows, self.num_qo_heads, self.head_dim), dtype=self.dtype,
+                              device=self.device)
+        elif (out.dtype != self.dtype or out.dim() != 3 or not out.is_contiguous()
+              or tuple(out.shape[1:]) != (self.num_qo_heads, self.head_dim)):
+            raise PkvError(PKV_ELAYOUT, "out: expected a packed [rows, num_qo_heads, head_dim] "
+                                        "tensor of the plan's dtype")
+        if lse is None and return_lse:
+            lse = torch.empty((rows, self.num_qo_heads), dtype=torch.float32, device=self.device)
+        elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                                  or lse.dim() != 2 or lse.shape[1] != self.num_qo_heads
+                                  or lse.shape[0] < rows):
+            raise PkvError(PKV_ELAYOUT, "lse: expected a packed fp32 [rows, num_qo_heads] tensor")
+        code = _dtype_code(self.dtype)
+        _check(_lib.pkv_run(
+            self._h, q.data_ptr(), q.shape[0], q.shape[1], q.shape[2], q.stride(0), q.stride(1),
+            k.data_ptr(), k.shape[0], k.shape[1], k.shape[2], k.shape[3],
+            k.stride(0), k.stride(1), k.stride(2),
+            v.data_ptr(), v.shape[0], v.shape[1], v.shape[2], v.shape[3],
+            v.stride(0), v.stride(1), v.stride(2),
+            code, out.data_ptr(), out.shape[0], lse.data_ptr() if lse is not None else None,
+            self._stream(stream)))
+        return out, lse
+
+    def debug_gather(self, paged_k, paged_v, kv_layout="NHD", stream=None):
+        """Logical K and V rows [sum kv_len, Hkv, D] read through the kernel's page path."""
+        torch = _torch()
+        k = self._cache_view(paged_k, kv_layout)
+        v = self._cache_view(paged_v, kv_layout)
+        total = int(self._kv_total)
+        ko = torch.empty((total, self.num_kv_heads, self.head_dim), dtype=self.dtype,
+                         device=self.device)
+        vo = torch.empty_like(ko)
+        _check(_lib.pkv_debug_gather(
+            self._h, k.data_ptr(), k.shape[0], k.shape[1], k.shape[2], k.shape[3],
+            k.stride(0), k.stride(1), k.stride(2),
+            v.data_ptr(), v.shape[0], v.shape[1], v.shape[2], v.shape[3],
+            v.stride(0), v.stride(1), v.stride(2),
+            _dtype_code(self.dtype), ko.data_ptr(), vo.data_ptr(), total, self._stream(stream)))
+        return ko, vo
+
+
+def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
+               num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype, device,
+               host_only, stream, opts):
+    lib = load_library()
+    qo, kv, idx, last, batch = _plan_arrays(qo_indptr, kv_indptr, kv_page_indices,
+                                            kv_last_page_len)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(head_dim)
+    code = _dtype_code(dtype)
+    o = _options(**opts)
+    args = (_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), _ptr_i32(last), batch,
+            int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
+            int(bool(causal)), int(window_left))
+    handle = ctypes.c_void_p()
+    int_ws = float_ws = None
+    torch = _torch()
+    tdtype = {PKV_BF16: torch.bfloat16, PKV_FP16: torch.float16}.get(code)
+    if host_only:
+        _check(lib.pkv_plan(*args, ctypes.c_float(sm_scale), code, None, 0, None, 0, None,
+                            ctypes.byref(o), ctypes.byref(handle)))
+        dev = None
+    else:
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        ib, fb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(lib.pkv_workspace_size(*args, ctypes.byref(o), ctypes.byref(ib), ctypes.byref(fb)))
+        int_ws = torch.empty(max(ib.value, 256), dtype=torch.uint8, device=dev)
+        float_ws = torch.empty(max(fb.value // 4, 64), dtype=torch.float32, device=dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        _check(lib.pkv_plan(*args, ctypes.c_float(sm_scale), code, int_ws.data_ptr(),
+                            int_ws.numel(), float_ws.data_ptr(), float_ws.numel() * 4,
+                            ctypes.c_void_p(s.cuda_stream), ctypes.byref(o),
+                            ctypes.byref(handle)))
+    p = Plan(handle.value, tdtype, int(head_dim), int(num_qo_heads), int(num_kv_heads),
+             int(page_size), dev, int_ws, float_ws)
+    nb = np.diff(kv.astype(np.int64)) if batch > 0 else np.zeros(0, dtype=np.int64)
+    lens = np.where(nb > 0, (nb - 1) * int(page_size) + last.astype(np.int64), 0)
+    p._kv_total = int(lens.sum())
+    return p
+
+
+def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, num_kv_heads,
+         head_dim, page_size, causal, window_left=-1, sm_scale=None, dtype="bf16",
+         device="cuda", stream=None, num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0):
+    """Validate and schedule a batch; returns a runnable Plan.
+
+    Host int arrays: qo_indptr[B+1], kv_indptr[B+1], kv_page_indices[kv_indptr[B]],
+    kv_last_page_len[B].  sm_scale defaults to 1/sqrt(head_dim).
+    num_kv_chunks / kv_begin / kv_end / tile: optional scheduling knobs (see include/pkv.h).
+    """
+    return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
+                      num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
+                      device, False, stream,
+                      dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
+                           tile=tile))
+
+
+def plan_host(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
+              num_kv_heads, head_dim, page_size, causal, window_left=-1, sm_scale=None,
+              dtype="bf16", num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0):
+    """Validate and schedule without a device: an inspectable, non-runnable Plan."""
+    return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
+                      num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
+                      None, True, None,
+                      dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
+                           tile=tile))
+
+
+def verify_plan(kv_indptr, kv_page_indices, kv_last_page_len, q_len_per_req, num_qo_heads,
+                num_kv_heads, head_dim, page_size, sm_scale=None, dtype="bf16", device="cuda",
+                **opts):
+    """Chain speculative-decode verify: a causal prefill with q_len_per_req rows per request
+    (PR #362: qo_indptr advances by the draft length, the mask is bottom-right causal)."""
+    batch = len(_host_i32(kv_indptr, "kv_indptr")) - 1
+    qo = np.arange(batch + 1, dtype=np.int64) * int(q_len_per_req)
+    return plan(qo, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, num_kv_heads,
+                head_dim, page_size, True, -1, sm_scale, dtype, device, **opts)
+
+
+def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """Combine two partial states over disjoint key sets -> (o, lse).
+
+    o_*: packed [rows, heads, head_dim] fp16/bf16/fp32; lse_*: packed fp32 [rows, heads].
+    out / lse_out may be o_a / lse_a for an in-place merge."""
+    torch = _torch()
+    lib = load_library()
+    if o_a.shape != o_b.shape or o_a.dtype != o_b.dtype or o_a.dim() != 3:
+        raise PkvError(PKV_EMISMATCH, f"o_a / o_b: expected equal [rows, heads, dim] shapes and "
+                                      f"dtypes, given {tuple(o_a.shape)} {o_a.dtype} and "
+                                      f"{tuple(o_b.shape)} {o_b.dtype}")
+    rows, heads, dim = o_a.shape
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (rows, heads):
+            raise PkvError(PKV_EMISMATCH, f"{name}: expected fp32 [{rows}, {heads}], given "
+                                          f"{t.dtype} {tuple(t.shape)}")
+    for name, t in (("o_a", o_a), ("o_b", o_b), ("lse_a", lse_a), ("lse_b", lse_b)):
+        if not t.is_contiguous():
+            raise PkvError(PKV_ELAYOUT, f"{name}: expected a packed tensor")
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    if out.shape != o_a.shape or out.dtype != o_a.dtype or not out.is_contiguous():
+        raise PkvError(PKV_ELAYOUT, "out: expected a packed tensor shaped like o_a")
+    if tuple(lse_out.shape) != (rows, heads) or not lse_out.is_contiguous():
+        raise PkvError(PKV_ELAYOUT, "lse_out: expected a packed fp32 [rows, heads] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(o_a.device)
+    _check(lib.pkv_merge_states(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                lse_b.data_ptr(), out.data_ptr(), lse_out.data_ptr(), rows,
+                                heads, dim, _dtype_code(o_a.dtype),
+                                ctypes.c_void_p(stream.cuda_stream)))
+    return out, lse_out

@@ -1,0 +1,719 @@
+// Host side of the paged-KV attention prefill library: argument validation,
+// the scheduler that turns a batch into work-group tasks, and the C ABI.
+//
+// Sources (web pages of the AMD-Ecosystem FlashInfer fork):
+//   PR #362 "Support speculative-decode verify on ROCm, and stop auto routing
+//     short-query prefill to AITER", Review notes: kv_len is derived from the
+//     paged metadata (kv_indptr and last_page_len), and a causal request whose
+//     kv_len is below its qo_len gives a silently wrong answer on the batch
+//     paged path.  Architecture notes: the graph-mode row bound
+//     total_num_rows - batch_size + 1 inflates tiles; this planner sees every
+//     request's lengths and needs no such bound.
+//   PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
+//     What changed: a window at least as wide as the sequence is normalised
+//     to -1 (with a signed compare); the batch planner there could not do it
+//     per request because it knew only the maximum kv_len.  This one does.
+//   PR #399 "Refuse attention inputs the ROCm kernels would compute
+//     wrongly", What changed / Architecture notes: strided last dimensions,
+//     head counts the GQA group cannot divide (and zero kv heads), and run()
+//     tensors that disagree with plan() are refused; token counts are
+//     minimums because graph callers pad; validation precedes the first
+//     write so a rejected plan leaves earlier plans usable; the plan keeps its
+//     own copy of every host array (a kept view of a caller's CPU indptr gave
+//     wrong answers there).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+const char* dtype_name(int d) {
+  return d == PKV_FP16 ? "fp16" : d == PKV_BF16 ? "bf16" : d == PKV_FP32 ? "fp32" : "unknown";
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kNumCUs = 256;               // MI355X compute units
+constexpr int kTargetTasks = 2 * kNumCUs;  // work groups wanted per launch
+
+struct Schedule {
+  int32_t batch = 0, hq = 0, hkv = 0, group = 0, head_dim = 0, page_size = 0;
+  int32_t causal = 0, window_left = -1, tile_kind = 0, rows = 0, keys = 0;
+  int64_t total_q = 0, num_indices = 0, total_kv = 0;
+  int32_t max_page = -1, max_kv_len = 0, num_slots = 0;
+  std::vector<ReqInfo> reqs;
+  std::vector<WorkItem> work;
+  std::vector<MergeItem> merges;
+  // int workspace layout
+  size_t off_reqs = 0, off_work = 0, off_merge = 0, off_pages = 0, int_bytes = 0;
+  // float workspace layout
+  size_t off_part_lse = 0, float_bytes = 0;
+};
+
+struct RowTask {
+  int32_t b, kvh, row0, nrows;
+  int32_t key_lo, key_hi;  // inclusive visible key range of the task (key_lo > key_hi: none)
+  int32_t tile_begin;
+};
+
+pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                    int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t page_size,
+                    int32_t causal, int32_t window_left, const pkv_plan_options* opts,
+                    Schedule* S) {
+  if (batch < 0) return fail(PKV_EINVAL, "batch_size: expected >= 0, given %d", batch);
+  if (hkv <= 0)
+    return fail(PKV_EGQA, "num_kv_heads: expected a positive head count, given %d", hkv);
+  if (hq <= 0 || hq % hkv != 0)
+    return fail(PKV_EGQA,
+                "num_qo_heads: expected a positive multiple of num_kv_heads=%d, given %d", hkv,
+                hq);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_EINVAL, "head_dim: expected 64 or 128, given %d", head_dim);
+  if (page_size < 1) return fail(PKV_EINVAL, "page_size: expected >= 1, given %d", page_size);
+  if (causal != 0 && causal != 1)
+    return fail(PKV_EINVAL, "causal: expected 0 or 1, given %d", causal);
+  if (window_left < -1)
+    return fail(PKV_EINVAL, "window_left: expected -1 (no window) or >= 0, given %d",
+                window_left);
+  if (batch > 0 && (!qo_indptr || !kv_indptr || !kv_last_page_len))
+    return fail(PKV_EINVAL, "qo_indptr / kv_indptr / kv_last_page_len: expected host arrays, "
+                            "given NULL");
+  pkv_plan_options o{};
+  o.kv_end = -1;
+  if (opts) o = *opts;
+  if (o.num_kv_chunks < 0)
+    return fail(PKV_EINVAL, "opts.num_kv_chunks: expected >= 0, given %d", o.num_kv_chunks);
+  if (o.kv_begin < 0) return fail(PKV_EINVAL, "opts.kv_begin: expected >= 0, given %d", o.kv_begin);
+  if (o.kv_end >= 0 && o.kv_end < o.kv_begin)
+    return fail(PKV_EINVAL, "opts.kv_end: expected >= kv_begin=%d or < 0, given %d", o.kv_begin,
+                o.kv_end);
+  if (o.tile < 0 || o.tile > 2) return fail(PKV_EINVAL, "opts.tile: expected 0, 1 or 2, given %d", o.tile);
+  const int64_t opt_end = o.kv_end < 0 ? INT64_MAX : o.kv_end;
+
+  const int32_t qi0 = batch > 0 ? qo_indptr[0] : 0;
+  const int32_t ki0 = batch > 0 ? kv_indptr[0] : 0;
+  if (qi0 != 0) return fail(PKV_EINVAL, "qo_indptr[0]: expected 0, given %d", qi0);
+  if (ki0 != 0) return fail(PKV_EINVAL, "kv_indptr[0]: expected 0, given %d", ki0);
+
+  S->batch = batch;
+  S->hq = hq;
+  S->hkv = hkv;
+  S->group = hq / hkv;
+  S->head_dim = head_dim;
+  S->page_size = page_size;
+  S->causal = causal;
+  S->window_left = window_left;
+  S->reqs.assign(batch, ReqInfo{});
+  int64_t max_rows = 0, kv_acc = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t ql = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    const int64_t np = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+    if (ql < 0)
+      return fail(PKV_EINVAL, "qo_indptr[%d]: expected >= qo_indptr[%d]=%d, given %d", b + 1, b,
+                  qo_indptr[b], qo_indptr[b + 1]);
+    if (np < 0)
+      return fail(PKV_EINVAL, "kv_indptr[%d]: expected >= kv_indptr[%d]=%d, given %d", b + 1, b,
+                  kv_indptr[b], kv_indptr[b + 1]);
+    int64_t L = 0;
+    if (np > 0) {
+      const int32_t last = kv_last_page_len[b];
+      if (last < 1 || last > page_size)
+        return fail(PKV_EINVAL, "kv_last_page_len[%d]: expected in [1, page_size=%d], given %d",
+                    b, page_size, last);
+      L = (np - 1) * page_size + last;
+    }
+    if (L > INT32_MAX / 2)
+      return fail(PKV_EINVAL, "kv_len of request %d: expected < 2^30, given %lld", b,
+                  (long long)L);
+    if (ql > 0 && L == 0)
+      return fail(PKV_EINVAL, "request %d: expected kv_len >= 1 for qo_len=%lld, given kv_len=0",
+                  b, (long long)ql);
+    if (causal && L < ql)
+      return fail(PKV_EINVAL,
+                  "request %d: causal mask needs kv_len >= qo_len=%lld, given kv_len=%lld", b,
+                  (long long)ql, (long long)L);
+    if (ql * S->group > INT32_MAX / 2)
+      return fail(PKV_EINVAL, "request %d: qo_len * group too large (%lld)", b,
+                  (long long)(ql * S->group));
+    ReqInfo& r = S->reqs[b];
+    r.qo_start = qo_indptr[b];
+    r.qo_len = (int32_t)ql;
+    r.kv_len = (int32_t)L;
+    r.page_off = kv_indptr[b];
+    // A window of kv_len - 1 or more keeps every key (j >= i - qo_len + 1 - ...
+    // <= 0 for every row): normalise it away per request, signed compare.
+    r.window = (window_left >= 0 && (int64_t)window_left < L - 1) ? window_left : -1;
+    r.kv_out_start = (int32_t)kv_acc;
+    kv_acc += L;
+    S->max_kv_len = std::max<int32_t>(S->max_kv_len, (int32_t)L);
+    max_rows = std::max<int64_t>(max_rows, ql * S->group);
+  }
+  S->total_q = batch > 0 ? qo_indptr[batch] : 0;
+  S->num_indices = batch > 0 ? kv_indptr[batch] : 0;
+  S->total_kv = kv_acc;
+  if (S->num_indices > 0 && !kv_page_indices)
+    return fail(PKV_EINVAL, "kv_page_indices: expected %lld entries, given NULL",
+                (long long)S->num_indices);
+  for (int64_t i = 0; i < S->num_indices; ++i) {
+    const int32_t p = kv_page_indices[i];
+    if (p < 0) return fail(PKV_EINVAL, "kv_page_indices[%lld]: expected >= 0, given %d", (long long)i, p);
+    S->max_page = std::max(S->max_page, p);
+  }
+
+  // ---- tile shape
+  int kind;
+  if (o.tile == 1) kind = TILE_PREFILL;
+  else if (o.tile == 2) kind = max_rows <= 16 ? TILE_SHORT16 : TILE_SHORT32;
+  else kind = max_rows <= 16 ? TILE_SHORT16 : (max_rows <= 32 ? TILE_SHORT32 : TILE_PREFILL);
+  S->tile_kind = kind;
+  S->rows = tile_rows(kind);
+  S->keys = tile_keys(kind);
+  const int MR = S->rows, NK = S->keys, G = S->group;
+
+  // ---- row tasks with their visible key ranges
+  std::vector<RowTask> tasks;
+  for (int32_t b = 0; b < batch; ++b) {
+    const ReqInfo& r = S->reqs[b];
+    const int32_t R = r.qo_len * G;
+    const int32_t sh = r.kv_len - r.qo_len;
+    for (int32_t kvh = 0; kvh < hkv; ++kvh) {
+      for (int32_t row0 = 0; row0 < R; row0 += MR) {
+        RowTask t;
+        t.b = b;
+        t.kvh = kvh;
+        t.row0 = row0;
+        t.nrows = std::min(MR, R - row0);
+        const int32_t pmin = row0 / G, pmax = (row0 + t.nrows - 1) / G;
+        int64_t lo = r.window >= 0 ? std::max<int64_t>(0, (int64_t)pmin + sh - r.window) : 0;
+        int64_t hi = causal ? (int64_t)pmax + sh : (int64_t)r.kv_len - 1;
+        hi = std::min<int64_t>(hi, r.kv_len - 1);
+        lo = std::max<int64_t>(lo, o.kv_begin);
+        hi = std::min<int64_t>(hi, opt_end - 1);
+        t.key_lo = (int32_t)std::min<int64_t>(lo, INT32_MAX / 2);
+        t.key_hi = (int32_t)std::max<int64_t>(hi, -1);
+        t.tile_begin = t.key_lo <= t.key_hi ? t.key_lo / NK * NK : 0;
+        tasks.push_back(t);
+      }
+    }
+  }
+
+  // ---- split decision
+  auto cost = [&](const RowTask& t) -> int64_t {
+    return t.key_lo > t.key_hi ? 0 : (t.key_hi + 1 - t.tile_begin + NK - 1) / NK;
+  };
+  int64_t chunk_tiles = 0;  // 0: no automatic split
+  if (o.num_kv_chunks == 0 && (int64_t)tasks.size() < kTargetTasks) {
+    int64_t total = 0;
+    for (const RowTask& t : tasks) total += cost(t);
+    const int64_t min_tiles = (kind == TILE_PREFILL) ? 8 : 4;
+    chunk_tiles = std::max<int64_t>(min_tiles, (total + kTargetTasks - 1) / kTargetTasks);
+  }
+
+  std::vector<std::pair<int64_t, WorkItem>> items;  // (cost, item)
+  auto emit = [&](const RowTask& t, int32_t lo, int32_t end, int32_t tb, int32_t slot) {
+    WorkItem w;
+    w.b = t.b;
+    w.kvh = t.kvh;
+    w.row0 = t.row0;
+    w.nrows = t.nrows;
+    w.key_lo = lo;
+    w.kv_end = end;
+    w.slot = slot;
+    w.tile_begin = tb;
+    const int64_t c = end > tb ? (end - tb + NK - 1) / NK : 0;
+    items.emplace_back(c, w);
+  };
+  int32_t slots = 0;
+  for (const RowTask& t : tasks) {
+    if (t.key_lo > t.key_hi) {  // nothing visible (only with a key-range option)
+      emit(t, 0, 0, 0, -1);
+      continue;
+    }
+    std::vector<std::pair<int32_t, int32_t>> chunks;  // [c0, c1) key ranges
+    if (o.num_kv_chunks > 0) {
+      const int64_t L = S->reqs[t.b].kv_len;
+      int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
+      clen = std::max<int64_t>(NK, (clen + NK - 1) / NK * NK);
+      for (int64_t c0 = 0; c0 < L; c0 += clen) {
+        const int64_t a = std::max<int64_t>(c0, t.key_lo);
+        const int64_t e = std::min<int64_t>(c0 + clen, (int64_t)t.key_hi + 1);
+        if (a < e) chunks.emplace_back((int32_t)a, (int32_t)e);
+      }
+    } else if (chunk_tiles > 0 && cost(t) > chunk_tiles) {
+      const int64_t step = chunk_tiles * NK;
+      for (int64_t c0 = t.tile_begin; c0 <= t.key_hi; c0 += step) {
+        const int64_t a = std::max<int64_t>(c0, t.key_lo);
+        const int64_t e = std::min<int64_t>(c0 + step, (int64_t)t.key_hi + 1);
+        if (a < e) chunks.emplace_back((int32_t)a, (int32_t)e);
+      }
+    } else {
+      chunks.emplace_back(t.key_lo, t.key_hi + 1);
+    }
+    if (chunks.size() == 1) {
+      emit(t, chunks[0].first, chunks[0].second, t.tile_begin, -1);
+      continue;
+    }
+    MergeItem m;
+    m.b = t.b;
+    m.kvh = t.kvh;
+    m.row0 = t.row0;
+    m.nrows = t.nrows;
+    m.slot0 = slots;
+    m.nslots = (int32_t)chunks.size();
+    m.pad0 = m.pad1 = 0;
+    S->merges.push_back(m);
+    for (const auto& c : chunks) {
+      const int32_t tb = std::max(t.tile_begin, c.first / NK * NK);
+      emit(t, c.first, c.second, tb, slots++);
+    }
+  }
+  S->num_slots = slots;
+  // Longest tasks first so the tail of the launch is made of short ones.
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::pair<int64_t, WorkItem>& x, const std::pair<int64_t, WorkItem>& y) {
+                     return x.first > y.first;
+                   });
+  S->work.clear();
+  S->work.reserve(items.size());
+  for (const auto& it : items) S->work.push_back(it.second);
+  if (S->work.size() > (size_t)INT32_MAX / 2)
+    return fail(PKV_EINVAL, "batch too large: %zu tasks", S->work.size());
+
+  // ---- workspace layouts
+  size_t off = 0;
+  S->off_reqs = off;
+  off = align_up(off + S->reqs.size() * sizeof(ReqInfo), 256);
+  S->off_work = off;
+  off = align_up(off + S->work.size() * sizeof(WorkItem), 256);
+  S->off_merge = off;
+  off = align_up(off + S->merges.size() * sizeof(MergeItem), 256);
+  S->off_pages = off;
+  off = align_up(off + (size_t)S->num_indices * sizeof(int32_t), 256);
+  S->int_bytes = std::max<size_t>(off, 256);
+  const size_t part_o = (size_t)slots * MR * head_dim * sizeof(float);
+  S->off_part_lse = align_up(part_o, 256);
+  S->float_bytes = slots > 0 ? align_up(S->off_part_lse + (size_t)slots * MR * sizeof(float), 256) : 0;
+  return PKV_OK;
+}
+
+// ---- pinned staging buffers for the one host-to-device copy per plan --------
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  int device = -1;
+  bool in_flight = false;
+};
+std::mutex g_staging_mu;
+std::vector<Staging*> g_staging;
+
+pkv_status copy_to_device(void* dst, const std::vector<uint8_t>& src, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  Staging* s = nullptr;
+  for (Staging* c : g_staging) {
+    if (c->device != dev || c->cap < src.size()) continue;
+    if (c->in_flight && hipEventQuery(c->ev) != hipSuccess) continue;
+    s = c;
+    break;
+  }
+  if (!s) {
+    s = new Staging();
+    s->device = dev;
+    s->cap = std::max<size_t>(src.size(), 1 << 16);
+    e = hipHostMalloc(&s->host, s->cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      delete s;
+      return fail(PKV_EHIP, "hipHostMalloc(%zu): %s", src.size(), hipGetErrorString(e));
+    }
+    e = hipEventCreateWithFlags(&s->ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipHostFree(s->host);
+      delete s;
+      return fail(PKV_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+    g_staging.push_back(s);
+  }
+  std::memcpy(s->host, src.data(), src.size());
+  e = hipMemcpyAsync(dst, s->host, src.size(), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(PKV_EHIP, "hipMemcpyAsync(plan): %s", hipGetErrorString(e));
+  e = hipEventRecord(s->ev, stream);
+  if (e != hipSuccess) return fail(PKV_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+  s->in_flight = true;
+  return PKV_OK;
+}
+
+}  // namespace
+
+struct pkv_plan_s {
+  Schedule S;
+  pkv_dtype dtype;
+  float sm_scale;
+  int32_t page_shift;
+  uint8_t* int_ws = nullptr;
+  float* float_ws = nullptr;
+  bool has_device_copy = false;
+};
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                              const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                              int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t causal,
+                              int32_t window_left, const pkv_plan_options* opts,
+                              size_t* int_ws_bytes, size_t* float_ws_bytes) {
+  g_err.clear();
+  Schedule S;
+  pkv_status st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
+                           num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
+                           opts, &S);
+  if (st != PKV_OK) return st;
+  if (int_ws_bytes) *int_ws_bytes = S.int_bytes;
+  if (float_ws_bytes) *float_ws_bytes = S.float_bytes;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                    int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t causal, int32_t window_left,
+                    float sm_scale, pkv_dtype dtype, void* int_ws, size_t int_ws_bytes,
+                    void* float_ws, size_t float_ws_bytes, void* stream,
+                    const pkv_plan_options* opts, pkv_plan_t* out_plan) {
+  g_err.clear();
+  if (!out_plan) return fail(PKV_EINVAL, "out_plan: expected a pointer, given NULL");
+  *out_plan = nullptr;
+  if (dtype != PKV_FP16 && dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "dtype: expected fp16 or bf16, given %s", dtype_name(dtype));
+  if (!std::isfinite(sm_scale))
+    return fail(PKV_EINVAL, "sm_scale: expected a finite value, given %g", (double)sm_scale);
+  pkv_plan_s* p = new pkv_plan_s();
+  pkv_status st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
+                           num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
+                           opts, &p->S);
+  if (st != PKV_OK) {
+    delete p;
+    return st;
+  }
+  const Schedule& S = p->S;
+  p->dtype = dtype;
+  p->sm_scale = sm_scale;
+  p->page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0) {
+    int sh = 0;
+    while ((1 << sh) < page_size) ++sh;
+    p->page_shift = sh;
+  }
+  const bool dry = (int_ws == nullptr && int_ws_bytes == 0);
+  if (!dry) {
+    if (!int_ws || int_ws_bytes < S.int_bytes) {
+      delete p;
+      return fail(PKV_EWORKSPACE, "int_ws: expected >= %zu bytes, given %zu%s", S.int_bytes,
+                  int_ws_bytes, int_ws ? "" : " (NULL)");
+    }
+    if (reinterpret_cast<uintptr_t>(int_ws) % 256 != 0) {
+      delete p;
+      return fail(PKV_ELAYOUT, "int_ws: expected 256-byte alignment");
+    }
+    if (S.float_bytes > 0 && (!float_ws || float_ws_bytes < S.float_bytes)) {
+      delete p;
+      return fail(PKV_EWORKSPACE, "float_ws: expected >= %zu bytes, given %zu%s", S.float_bytes,
+                  float_ws_bytes, float_ws ? "" : " (NULL)");
+    }
+    if (S.float_bytes > 0 && reinterpret_cast<uintptr_t>(float_ws) % 256 != 0) {
+      delete p;
+      return fail(PKV_ELAYOUT, "float_ws: expected 256-byte alignment");
+    }
+    std::vector<uint8_t> blob(S.int_bytes, 0);
+    std::memcpy(blob.data() + S.off_reqs, S.reqs.data(), S.reqs.size() * sizeof(ReqInfo));
+    std::memcpy(blob.data() + S.off_work, S.work.data(), S.work.size() * sizeof(WorkItem));
+    std::memcpy(blob.data() + S.off_merge, S.merges.data(), S.merges.size() * sizeof(MergeItem));
+    if (S.num_indices > 0)
+      std::memcpy(blob.data() + S.off_pages, kv_page_indices, S.num_indices * sizeof(int32_t));
+    st = copy_to_device(int_ws, blob, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) {
+      delete p;
+      return st;
+    }
+    p->int_ws = static_cast<uint8_t*>(int_ws);
+    p->float_ws = static_cast<float*>(float_ws);
+    p->has_device_copy = true;
+  }
+  *out_plan = p;
+  return PKV_OK;
+}
+
+void pkv_plan_destroy(pkv_plan_t plan) { delete plan; }
+
+pkv_status pkv_plan_get_info(pkv_plan_t p, pkv_plan_info* info) {
+  g_err.clear();
+  if (!p) return fail(PKV_ENOTPLANNED, "plan: expected a plan handle, given NULL");
+  if (!info) return fail(PKV_EINVAL, "info: expected a pointer, given NULL");
+  const Schedule& S = p->S;
+  info->total_q_rows = S.total_q;
+  info->num_page_indices = S.num_indices;
+  info->batch_size = S.batch;
+  info->num_work_items = (int32_t)S.work.size();
+  info->num_merge_items = (int32_t)S.merges.size();
+  info->num_partial_slots = S.num_slots;
+  info->tile_rows = S.rows;
+  info->tile_keys = S.keys;
+  info->max_page_index = S.max_page;
+  info->has_device_copy = p->has_device_copy ? 1 : 0;
+  info->int_ws_bytes = (int64_t)S.int_bytes;
+  info->float_ws_bytes = (int64_t)S.float_bytes;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_get_work(pkv_plan_t p, int32_t* out, int64_t capacity, int64_t* count) {
+  g_err.clear();
+  if (!p) return fail(PKV_ENOTPLANNED, "plan: expected a plan handle, given NULL");
+  const auto& W = p->S.work;
+  if (count) *count = (int64_t)W.size();
+  if (!out) return PKV_OK;
+  const int64_t n = std::min<int64_t>(capacity, (int64_t)W.size());
+  for (int64_t i = 0; i < n; ++i) {
+    const WorkItem& w = W[i];
+    int32_t* r = out + 8 * i;
+    r[0] = w.b;
+    r[1] = w.kvh;
+    r[2] = w.row0;
+    r[3] = w.nrows;
+    r[4] = w.key_lo;
+    r[5] = w.kv_end;
+    r[6] = w.slot;
+    r[7] = w.tile_begin;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+pkv_status check_cache(const pkv_plan_s* p, const char* name, const void* ptr, int64_t pages,
+                       int32_t psize, int32_t heads, int32_t dim, int64_t s_page, int64_t s_tok,
+                       int64_t s_head) {
+  const Schedule& S = p->S;
+  if (heads != S.hkv)
+    return fail(PKV_EMISMATCH, "%s num_kv_heads: planned %d, given %d", name, S.hkv, heads);
+  if (dim != S.head_dim)
+    return fail(PKV_EMISMATCH, "%s head_dim: planned %d, given %d", name, S.head_dim, dim);
+  if (psize != S.page_size)
+    return fail(PKV_EMISMATCH, "%s page_size: planned %d, given %d", name, S.page_size, psize);
+  if (S.max_page >= 0 && pages <= S.max_page)
+    return fail(PKV_EINVAL, "%s num_pages: page id %d is referenced, given a pool of %lld pages",
+                name, S.max_page, (long long)pages);
+  if (S.total_kv > 0 && !ptr) return fail(PKV_EINVAL, "%s: expected a device pointer, given NULL", name);
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+    return fail(PKV_ELAYOUT, "%s: expected 16-byte alignment", name);
+  if (s_page < 0 || s_tok < 0 || s_head < 0 || s_page % 8 || s_tok % 8 || s_head % 8)
+    return fail(PKV_ELAYOUT,
+                "%s strides (page %lld, token %lld, head %lld): expected non-negative multiples "
+                "of 8 elements with a packed head_dim",
+                name, (long long)s_page, (long long)s_tok, (long long)s_head);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads, int32_t q_dim,
+                   int64_t q_s_tok, int64_t q_s_head, const void* k, int64_t k_pages,
+                   int32_t k_page_size, int32_t k_heads, int32_t k_dim, int64_t k_s_page,
+                   int64_t k_s_tok, int64_t k_s_head, const void* v, int64_t v_pages,
+                   int32_t v_page_size, int32_t v_heads, int32_t v_dim, int64_t v_s_page,
+                   int64_t v_s_tok, int64_t v_s_head, pkv_dtype dtype, void* o, int64_t o_rows,
+                   float* lse, void* stream) {
+  g_err.clear();
+  if (!p) return fail(PKV_ENOTPLANNED, "plan: run before a successful plan");
+  if (!p->has_device_copy)
+    return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
+  const Schedule& S = p->S;
+  if (dtype != p->dtype)
+    return fail(PKV_EMISMATCH, "dtype: planned %s, given %s", dtype_name(p->dtype),
+                dtype_name(dtype));
+  if (q_heads != S.hq)
+    return fail(PKV_EMISMATCH, "q num_qo_heads: planned %d, given %d", S.hq, q_heads);
+  if (q_dim != S.head_dim)
+    return fail(PKV_EMISMATCH, "q head_dim: planned %d, given %d", S.head_dim, q_dim);
+  if (q_rows < S.total_q)
+    return fail(PKV_EMISMATCH, "q rows: planned at least %lld, given %lld", (long long)S.total_q,
+                (long long)q_rows);
+  if (o_rows < S.total_q)
+    return fail(PKV_EMISMATCH, "o rows: planned at least %lld, given %lld", (long long)S.total_q,
+                (long long)o_rows);
+  pkv_status st = check_cache(p, "k", k, k_pages, k_page_size, k_heads, k_dim, k_s_page, k_s_tok,
+                              k_s_head);
+  if (st != PKV_OK) return st;
+  st = check_cache(p, "v", v, v_pages, v_page_size, v_heads, v_dim, v_s_page, v_s_tok, v_s_head);
+  if (st != PKV_OK) return st;
+  if (S.total_q > 0) {
+    if (!q) return fail(PKV_EINVAL, "q: expected a device pointer, given NULL");
+    if (!o) return fail(PKV_EINVAL, "o: expected a device pointer, given NULL");
+  }
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return fail(PKV_ELAYOUT, "q: expected 16-byte alignment");
+  if (q_s_tok < 0 || q_s_head < 0 || q_s_tok % 8 || q_s_head % 8)
+    return fail(PKV_ELAYOUT,
+                "q strides (token %lld, head %lld): expected non-negative multiples of 8 "
+                "elements with a packed head_dim",
+                (long long)q_s_tok, (long long)q_s_head);
+  if (reinterpret_cast<uintptr_t>(o) % 16 != 0)
+    return fail(PKV_ELAYOUT, "o: expected 16-byte alignment");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(PKV_ELAYOUT, "lse: expected 4-byte alignment");
+  if (S.work.empty()) return PKV_OK;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.pages = reinterpret_cast<const int32_t*>(p->int_ws + S.off_pages);
+  a.reqs = reinterpret_cast<const ReqInfo*>(p->int_ws + S.off_reqs);
+  a.work = reinterpret_cast<const WorkItem*>(p->int_ws + S.off_work);
+  a.part_o = p->float_ws;
+  a.part_lse = p->float_ws ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p->float_ws) +
+                                                      S.off_part_lse)
+                           : nullptr;
+  a.q_s_tok = q_s_tok;
+  a.q_s_head = q_s_head;
+  a.k_s_page = k_s_page;
+  a.k_s_tok = k_s_tok;
+  a.k_s_head = k_s_head;
+  a.v_s_page = v_s_page;
+  a.v_s_tok = v_s_tok;
+  a.v_s_head = v_s_head;
+  a.num_work = (int32_t)S.work.size();
+  a.group = S.group;
+  a.num_qo_heads = S.hq;
+  a.page_size = S.page_size;
+  a.page_shift = p->page_shift;
+  a.causal = S.causal;
+  a.scale_log2 = p->sm_scale * 1.4426950408889634f;
+  hipError_t e = launch_attention(S.tile_kind, (int)p->dtype, S.head_dim, a, hs);
+  if (e != hipSuccess) return fail(PKV_EHIP, "attention launch: %s", hipGetErrorString(e));
+  if (!S.merges.empty()) {
+    SplitMergeArgs m;
+    m.o = o;
+    m.lse = lse;
+    m.reqs = a.reqs;
+    m.items = reinterpret_cast<const MergeItem*>(p->int_ws + S.off_merge);
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.num_items = (int32_t)S.merges.size();
+    m.group = S.group;
+    m.num_qo_heads = S.hq;
+    m.tile_rows = S.rows;
+    e = launch_split_merge((int)p->dtype, S.head_dim, m, hs);
+    if (e != hipSuccess) return fail(PKV_EHIP, "split merge launch: %s", hipGetErrorString(e));
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_merge_states(const void* o_a, const float* lse_a, const void* o_b,
+                            const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                            int32_t heads, int32_t head_dim, pkv_dtype dtype, void* stream) {
+  g_err.clear();
+  if (dtype != PKV_FP16 && dtype != PKV_BF16 && dtype != PKV_FP32)
+    return fail(PKV_EINVAL, "dtype: expected fp16, bf16 or fp32, given %d", (int)dtype);
+  if (rows < 0 || heads < 0 || head_dim < 0)
+    return fail(PKV_EINVAL, "shape [%lld, %d, %d]: expected non-negative sizes", (long long)rows,
+                heads, head_dim);
+  if (rows * heads > 0 && head_dim > 0 &&
+      (!o_a || !o_b || !o_out || !lse_a || !lse_b || !lse_out))
+    return fail(PKV_EINVAL, "merge_states: expected device pointers, given NULL");
+  hipError_t e = launch_merge_states((int)dtype, o_a, lse_a, o_b, lse_b, o_out, lse_out, rows,
+                                     heads, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "merge_states launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_t k_page_size,
+                            int32_t k_heads, int32_t k_dim, int64_t k_s_page, int64_t k_s_tok,
+                            int64_t k_s_head, const void* v, int64_t v_pages,
+                            int32_t v_page_size, int32_t v_heads, int32_t v_dim,
+                            int64_t v_s_page, int64_t v_s_tok, int64_t v_s_head,
+                            pkv_dtype dtype, void* k_out, void* v_out, int64_t out_rows,
+                            void* stream) {
+  g_err.clear();
+  if (!p) return fail(PKV_ENOTPLANNED, "plan: debug_gather before a successful plan");
+  if (!p->has_device_copy)
+    return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
+  const Schedule& S = p->S;
+  if (dtype != p->dtype)
+    return fail(PKV_EMISMATCH, "dtype: planned %s, given %s", dtype_name(p->dtype),
+                dtype_name(dtype));
+  pkv_status st = check_cache(p, "k", k, k_pages, k_page_size, k_heads, k_dim, k_s_page, k_s_tok,
+                              k_s_head);
+  if (st != PKV_OK) return st;
+  st = check_cache(p, "v", v, v_pages, v_page_size, v_heads, v_dim, v_s_page, v_s_tok, v_s_head);
+  if (st != PKV_OK) return st;
+  if (out_rows < S.total_kv)
+    return fail(PKV_EMISMATCH, "gather rows: planned at least %lld, given %lld",
+                (long long)S.total_kv, (long long)out_rows);
+  if (S.total_kv > 0 && (!k_out || !v_out))
+    return fail(PKV_EINVAL, "k_out / v_out: expected device pointers, given NULL");
+  if (reinterpret_cast<uintptr_t>(k_out) % 16 || reinterpret_cast<uintptr_t>(v_out) % 16)
+    return fail(PKV_ELAYOUT, "k_out / v_out: expected 16-byte alignment");
+  GatherArgs g;
+  g.k = k;
+  g.v = v;
+  g.k_out = k_out;
+  g.v_out = v_out;
+  g.pages = reinterpret_cast<const int32_t*>(p->int_ws + S.off_pages);
+  g.reqs = reinterpret_cast<const ReqInfo*>(p->int_ws + S.off_reqs);
+  g.k_s_page = k_s_page;
+  g.k_s_tok = k_s_tok;
+  g.k_s_head = k_s_head;
+  g.v_s_page = v_s_page;
+  g.v_s_tok = v_s_tok;
+  g.v_s_head = v_s_head;
+  g.num_kv_heads = S.hkv;
+  g.page_size = S.page_size;
+  g.page_shift = p->page_shift;
+  g.max_kv_len = S.max_kv_len;
+  g.batch = S.batch;
+  hipError_t e = launch_debug_gather((int)p->dtype, S.head_dim, g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "debug gather launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // extern "C"

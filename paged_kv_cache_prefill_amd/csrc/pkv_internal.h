@@ -1,0 +1,112 @@
+// Internal types shared by the host scheduler (pkv_host.cpp) and the HIP
+// kernels (pkv_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Per-request facts the kernels need (all derived and validated by plan).
+struct ReqInfo {
+  int32_t qo_start;      // first query row of the request in q / o
+  int32_t qo_len;        // query rows
+  int32_t kv_len;        // keys: (pages - 1) * page_size + last_page_len
+  int32_t page_off;      // first page-table entry of the request
+  int32_t window;        // window_left after normalisation (-1 = no window)
+  int32_t kv_out_start;  // first row of the request in a debug gather output
+  int32_t pad0, pad1;
+};
+
+// One work-group task: a tile of packed (position, head-in-group) rows of one
+// kv head of one request, against keys [tile_begin, kv_end) loaded tile by
+// tile; keys below key_lo or at/after kv_end are masked.  slot >= 0 sends the
+// result to fp32 partial slot `slot` (one chunk of a split query tile).
+struct WorkItem {
+  int32_t b, kvh, row0, nrows;
+  int32_t key_lo, kv_end, slot, tile_begin;
+};
+
+// A query tile whose keys were split over `nslots` consecutive partial slots.
+struct MergeItem {
+  int32_t b, kvh, row0, nrows;
+  int32_t slot0, nslots, pad0, pad1;
+};
+
+// Tile shapes the kernels are instantiated for.
+enum TileKind : int32_t {
+  TILE_PREFILL = 1,   // 4 waves along rows: 128 rows x 64 keys per iteration
+  TILE_SHORT16 = 2,   // 4 waves along keys: 16 rows x 128 keys per iteration
+  TILE_SHORT32 = 3,   // 4 waves along keys: 32 rows x 128 keys per iteration
+};
+
+inline int tile_rows(int kind) {
+  return kind == TILE_PREFILL ? 128 : (kind == TILE_SHORT16 ? 16 : 32);
+}
+inline int tile_keys(int kind) { return kind == TILE_PREFILL ? 64 : 128; }
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // nullable
+  const int32_t* pages;    // device copy of kv_page_indices
+  const ReqInfo* reqs;
+  const WorkItem* work;
+  float* part_o;           // [slots][tile_rows][head_dim] fp32
+  float* part_lse;         // [slots][tile_rows] fp32, log2 domain
+  int64_t q_s_tok, q_s_head;
+  int64_t k_s_page, k_s_tok, k_s_head;
+  int64_t v_s_page, v_s_tok, v_s_head;
+  int32_t num_work;
+  int32_t group;           // num_qo_heads / num_kv_heads
+  int32_t num_qo_heads;
+  int32_t page_size;
+  int32_t page_shift;      // log2(page_size) or -1
+  int32_t causal;
+  float scale_log2;        // sm_scale * log2(e)
+};
+
+struct SplitMergeArgs {
+  void* o;
+  float* lse;              // nullable
+  const ReqInfo* reqs;
+  const MergeItem* items;
+  const float* part_o;
+  const float* part_lse;
+  int32_t num_items;
+  int32_t group;
+  int32_t num_qo_heads;
+  int32_t tile_rows;
+};
+
+struct GatherArgs {
+  const void* k;
+  const void* v;
+  void* k_out;
+  void* v_out;
+  const int32_t* pages;
+  const ReqInfo* reqs;
+  int64_t k_s_page, k_s_tok, k_s_head;
+  int64_t v_s_page, v_s_tok, v_s_head;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t page_shift;
+  int32_t max_kv_len;
+  int32_t batch;
+};
+
+// dtype: 0 fp16, 1 bf16, 2 fp32 (merge_states only).
+hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                            hipStream_t stream);
+hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a,
+                              hipStream_t stream);
+hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,
+                               const void* o_b, const float* lse_b, void* o_out,
+                               float* lse_out, int64_t rows, int32_t heads,
+                               int32_t head_dim, hipStream_t stream);
+hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a,
+                               hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,651 @@
+// HIP kernels for paged-KV attention prefill on CDNA4 (gfx950).
+//
+// What is computed (web pages of the AMD-Ecosystem FlashInfer fork):
+//   - PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
+//     section "Why window_size_right stays -1": key j is kept for query row i
+//     when j + qo_len + window_left >= kv_len + i (left-only band, bottom-right
+//     anchored, independent of causal; -1 = no window).
+//   - PR #362 "Support speculative-decode verify on ROCm, ...", Summary: the
+//     causal mask is bottom-right aligned, j <= i + kv_len - qo_len, which is
+//     also chain speculative-verify semantics.
+//   - PR #399 "Refuse attention inputs the ROCm kernels would compute
+//     wrongly", What changed: q head h reads kv head h / (Hq / Hkv); o and lse
+//     are written packed; partial (o, lse) states are merged.
+//
+// Design (ours, for CDNA4; the pages describe an FA2-derived kernel only by
+// its tile rule):
+//   * A work-group task is a tile of packed rows (query position x q head of
+//     one GQA group, position-major) of one kv head.  Packing the group into
+//     the MFMA M dimension reads each K/V row once per kv head.
+//   * Keys are fetched straight through the page table: one 16-byte vector
+//     load per (key, 8 head-dim elements), coalesced along head_dim, staged
+//     through registers into a double-buffered LDS tile.  Nothing is gathered
+//     into a contiguous copy.
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_{bf16,f16} with fp32
+//     accumulation.  In that orientation each lane owns one query row (lane %
+//     16) in every MFMA result, so the row statistics stay per lane and the P
+//     fragment produced by the first MFMA is directly the B operand of the
+//     second (no shuffles); row max is reduced across the 4 lane groups with
+//     two xor-shuffles, the row sum only once at the end.
+//   * Softmax runs in the log2 domain (scale * log2 e folded into one
+//     multiply, hardware exp2); lse is converted to natural log on output.
+//   * Tiles entirely inside every row's visible band skip the mask; tiles
+//     outside the band are never visited (the scheduler clips key ranges).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <typename T>
+struct Traits;
+
+template <>
+struct Traits<__bf16> {
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mfma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Traits<_Float16> {
+  typedef f16x8 frag;
+  static __device__ __forceinline__ f32x4 mfma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) {
+  return static_cast<float>(x);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) {
+  return static_cast<T>(x);  // round to nearest even
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Element offset of (page-table slot of key j, head h, element 0) in a pool.
+__device__ __forceinline__ int64_t kv_offset(const int32_t* pages, int32_t page_off, int32_t j,
+                                             int32_t page_size, int32_t page_shift,
+                                             int64_t s_page, int64_t s_tok, int64_t s_head,
+                                             int32_t h) {
+  int32_t pidx, slot;
+  if (page_shift >= 0) {
+    pidx = j >> page_shift;
+    slot = j & (page_size - 1);
+  } else {
+    pidx = j / page_size;
+    slot = j - pidx * page_size;
+  }
+  const int64_t page = pages[page_off + pidx];
+  return page * s_page + (int64_t)slot * s_tok + (int64_t)h * s_head;
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+// WM waves split the rows, WN waves split the keys of each LDS tile;
+// each wave owns QB blocks of 16 rows and NW keys of the tile.
+template <typename T, int D, int WM, int WN, int QB, int NW>
+__global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
+  using Tr = Traits<T>;
+  using frag = typename Tr::frag;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int MW = 16 * QB;    // rows per wave
+  constexpr int NWG = NW * WN;   // keys per LDS tile
+  constexpr int CH = D / 8;      // 16-byte chunks per key row
+  constexpr int RP = CH + 1;     // LDS row pitch in chunks (one chunk of padding)
+  constexpr int NL = NWG * CH / NT;  // chunks each thread loads per tile (per K and V)
+  constexpr int DK = D / 32;     // MFMA k-steps over head_dim
+  constexpr int KB = NW / 16;    // 16-key blocks per wave
+  constexpr int DB = D / 16;     // 16-wide head_dim blocks of the output
+  static_assert(NWG * CH % NT == 0, "tile not divisible among threads");
+  static_assert(NW % 32 == 0, "wave key tile must be a multiple of 32");
+
+  __shared__ uint4 smem[2 * 2 * NWG * RP];
+  uint4* lds_k = smem;                 // [2][NWG][RP]
+  uint4* lds_v = smem + 2 * NWG * RP;  // [2][NWG][RP]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+
+  const WorkItem it = a.work[blockIdx.x];
+  const ReqInfo rq = a.reqs[it.b];
+  const int G = a.group;
+  const int R = rq.qo_len * G;          // packed rows of this (request, kv head)
+  const int shift_q = rq.kv_len - rq.qo_len;  // bottom-right offset L - Q
+  const int win = rq.window;
+
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ vp = static_cast<const T*>(a.v);
+
+  // ---- Q fragments (B operand of S^T = K Q^T) and per-row visible ranges
+  frag qf[QB][DK];
+  int lo[QB], hi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = it.row0 + wm * MW + qb * 16 + l16;
+    const bool valid = (r - it.row0) < it.nrows && r < R;
+    if (valid) {
+      const int pos = r / G;
+      const int h = it.kvh * G + (r - pos * G);
+      const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) {
+        uint4 u = *reinterpret_cast<const uint4*>(src + dk * 32 + g * 8);
+        qf[qb][dk] = __builtin_bit_cast(frag, u);
+      }
+      int l0 = 0;
+      if (win >= 0) l0 = max(0, pos + shift_q - win);
+      int h0 = a.causal ? pos + shift_q : rq.kv_len - 1;
+      lo[qb] = max(l0, it.key_lo);
+      hi[qb] = min(h0, it.kv_end - 1);
+    } else {
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) qf[qb][dk] = __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0));
+      lo[qb] = 1;
+      hi[qb] = 0;
+    }
+  }
+
+  // Range of keys every valid row of the task sees (tiles inside it need no mask).
+  int full_lo, full_hi;
+  {
+    const int rmax = min(it.row0 + it.nrows, R) - 1;
+    const int pmin = it.row0 / G;
+    const int pmax = rmax / G;
+    full_lo = (win >= 0) ? max(0, pmax + shift_q - win) : 0;
+    full_lo = max(full_lo, it.key_lo);
+    full_hi = a.causal ? pmin + shift_q : rq.kv_len - 1;
+    full_hi = min(full_hi, it.kv_end - 1);
+  }
+
+  // ---- accumulators
+  f32x4 oacc[DB][QB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int ntiles = it.kv_end > it.tile_begin ? (it.kv_end - it.tile_begin + NWG - 1) / NWG : 0;
+
+  uint4 kreg[NL], vreg[NL];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int c = tid + r * NT;
+      const int key = c / CH;
+      const int part = c - key * CH;
+      const int j = j0 + key;
+      if (j < it.kv_end) {
+        const int64_t ko = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift,
+                                     a.k_s_page, a.k_s_tok, a.k_s_head, it.kvh);
+        const int64_t vo = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift,
+                                     a.v_s_page, a.v_s_tok, a.v_s_head, it.kvh);
+        kreg[r] = *reinterpret_cast<const uint4*>(kp + ko + part * 8);
+        vreg[r] = *reinterpret_cast<const uint4*>(vp + vo + part * 8);
+      } else {
+        kreg[r] = make_uint4(0, 0, 0, 0);
+        vreg[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int c = tid + r * NT;
+      const int key = c / CH;
+      const int part = c - key * CH;
+      lds_k[(buf * NWG + key) * RP + part] = kreg[r];
+      lds_v[(buf * NWG + key) * RP + part] = vreg[r];
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(it.tile_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = it.tile_begin + t * NWG;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(j0 + NWG);
+
+    // ---- S^T = K Q^T for this wave's NW keys
+    f32x4 s[KB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint4* kt = lds_k + (buf * NWG + wn * NW) * RP;
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const frag af = __builtin_bit_cast(frag, kt[(kb * 16 + l16) * RP + dk * 4 + g]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(af, qf[qb][dk], s[kb][qb]);
+      }
+    }
+
+    // ---- scale, mask, online softmax (lane owns row l16 of each qb block,
+    // keys kb*16 + 4*g + i)
+    const int jw = j0 + wn * NW;
+    const bool full = (j0 >= full_lo) && (j0 + NWG - 1 <= full_hi);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[kb][qb][i] * a.scale_log2;
+          if (!full) {
+            const int j = jw + kb * 16 + 4 * g + i;
+            if (j < lo[qb] || j > hi[qb]) x = kNegInf;
+          }
+          s[kb][qb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[qb] - m_use);
+      m_run[qb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(s[kb][qb][i] - m_use);
+          s[kb][qb][i] = p;
+          rs += p;
+        }
+      }
+      l_run[qb] = l_run[qb] * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
+    // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, which is
+    // exactly where S^T put them; the A operand reads the same keys of V.
+    const T* vt = reinterpret_cast<const T*>(lds_v + (buf * NWG + wn * NW) * RP);
+#pragma unroll
+    for (int st = 0; st < NW / 32; ++st) {
+      frag pb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[qb][i] = from_f32<T>(s[2 * st][qb][i]);
+          pb[qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        frag af;
+        const int d = db * 16 + l16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = st * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+          af[e] = vt[key * RP * 8 + d];
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(af, pb[qb], oacc[db][qb]);
+      }
+    }
+
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  // Row sums were kept per lane; reduce over the 4 lane groups sharing a row.
+  float l_tot[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float x = l_run[qb] + __shfl_xor(l_run[qb], 16);
+    l_tot[qb] = x + __shfl_xor(x, 32);
+  }
+
+  T* __restrict__ op = static_cast<T*>(a.o);
+  const bool to_partial = it.slot >= 0;
+
+  if constexpr (WN == 1) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int rl = wm * MW + qb * 16 + l16;  // row within the task
+      const int r = it.row0 + rl;
+      if (rl >= it.nrows || r >= R) continue;
+      const float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+      const float lse2 = l_tot[qb] > 0.f ? m_run[qb] + fast_log2(l_tot[qb]) : kNegInf;
+      if (to_partial) {
+        float* dst = a.part_o + ((int64_t)it.slot * (WM * MW) + rl) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          f32x4 v = oacc[db][qb] * inv;
+          *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = v;
+        }
+        if (g == 0) a.part_lse[(int64_t)it.slot * (WM * MW) + rl] = lse2;
+      } else {
+        const int pos = r / G;
+        const int h = it.kvh * G + (r - pos * G);
+        const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+        T* dst = op + orow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          T o4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(oacc[db][qb][i] * inv);
+          *reinterpret_cast<uint2*>(dst + db * 16 + 4 * g) = *reinterpret_cast<uint2*>(o4);
+        }
+        if (g == 0 && a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+    }
+  } else {
+    // Waves along keys hold partial states of the same rows: combine in LDS.
+    static_assert(WM == 1, "key-split tiles use one row block");
+    float* red_m = reinterpret_cast<float*>(smem);       // [WN][MW]
+    float* red_l = red_m + WN * MW;                      // [WN][MW]
+    float* red_o = red_l + WN * MW;                      // [WN][MW][D]
+    static_assert((2 * WN * MW + WN * MW * D) * 4 <= (int)sizeof(smem), "LDS too small");
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (g == 0) {
+        red_m[wn * MW + qb * 16 + l16] = m_run[qb];
+        red_l[wn * MW + qb * 16 + l16] = l_tot[qb];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int rl = qb * 16 + l16;
+      float mt = kNegInf;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) mt = fmaxf(mt, red_m[w * MW + rl]);
+      const float mu = (mt == kNegInf) ? 0.f : mt;
+      const float sc = fast_exp2(m_run[qb] - mu);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x4 v = oacc[db][qb] * sc;
+        *reinterpret_cast<f32x4*>(red_o + ((wn * MW) + rl) * D + db * 16 + 4 * g) = v;
+      }
+    }
+    __syncthreads();
+    // Every thread finishes 4 consecutive head-dim elements of some rows.
+    for (int idx = tid; idx < MW * (D / 4); idx += NT) {
+      const int rl = idx / (D / 4);
+      const int d4 = idx - rl * (D / 4);
+      float mt = kNegInf;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) mt = fmaxf(mt, red_m[w * MW + rl]);
+      const float mu = (mt == kNegInf) ? 0.f : mt;
+      float lt = 0.f;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        lt += red_l[w * MW + rl] * fast_exp2(red_m[w * MW + rl] - mu);
+        acc += *reinterpret_cast<const f32x4*>(red_o + (w * MW + rl) * D + d4 * 4);
+      }
+      const int r = it.row0 + rl;
+      if (rl >= it.nrows || r >= R) continue;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse2 = lt > 0.f ? mt + fast_log2(lt) : kNegInf;
+      if (to_partial) {
+        float* dst = a.part_o + ((int64_t)it.slot * MW + rl) * D + d4 * 4;
+        *reinterpret_cast<f32x4*>(dst) = acc * inv;
+        if (d4 == 0) a.part_lse[(int64_t)it.slot * MW + rl] = lse2;
+      } else {
+        const int pos = r / G;
+        const int h = it.kvh * G + (r - pos * G);
+        const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+        T o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i] * inv);
+        *reinterpret_cast<uint2*>(op + orow * D + d4 * 4) = *reinterpret_cast<uint2*>(o4);
+        if (d4 == 0 && a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of split-KV partial states (N-way), one work group per split tile
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
+  const MergeItem it = a.items[blockIdx.x];
+  const ReqInfo rq = a.reqs[it.b];
+  const int G = a.group;
+  T* __restrict__ op = static_cast<T*>(a.o);
+  for (int idx = threadIdx.x; idx < it.nrows * (D / 4); idx += blockDim.x) {
+    const int rl = idx / (D / 4);
+    const int d4 = idx - rl * (D / 4);
+    float mt = kNegInf;
+    for (int c = 0; c < it.nslots; ++c)
+      mt = fmaxf(mt, a.part_lse[(int64_t)(it.slot0 + c) * a.tile_rows + rl]);
+    const float mu = (mt == kNegInf) ? 0.f : mt;
+    float wt = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < it.nslots; ++c) {
+      const int64_t sr = (int64_t)(it.slot0 + c) * a.tile_rows + rl;
+      const float w = fast_exp2(a.part_lse[sr] - mu);
+      wt += w;
+      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + sr * D + d4 * 4);
+    }
+    const float inv = wt > 0.f ? 1.f / wt : 0.f;
+    const int r = it.row0 + rl;
+    const int pos = r / G;
+    const int h = it.kvh * G + (r - pos * G);
+    const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+    T o4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i] * inv);
+    *reinterpret_cast<uint2*>(op + orow * D + d4 * 4) = *reinterpret_cast<uint2*>(o4);
+    if (d4 == 0 && a.lse != nullptr)
+      a.lse[orow] = (mt == kNegInf) ? kNegInf : (mt + fast_log2(wt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge_states: two partial states, natural-log lse
+// ---------------------------------------------------------------------------
+// In-place merges must not let one thread overwrite lse while another thread of
+// the same row still needs the old value: split the lse update into its own pass.
+__global__ __launch_bounds__(256) void merge_lse_kernel(const float* lse_a, const float* lse_b,
+                                                        float* lse_out, int64_t rowheads) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  for (int64_t rh = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; rh < rowheads;
+       rh += (int64_t)gridDim.x * blockDim.x) {
+    const float la = lse_a[rh], lb = lse_b[rh];
+    const float mt = fmaxf(la, lb);
+    if (mt == kNegInf) {
+      lse_out[rh] = kNegInf;
+    } else {
+      const float wt = fast_exp2((la - mt) * kLog2e) + fast_exp2((lb - mt) * kLog2e);
+      lse_out[rh] = mt + fast_log2(wt) * kLn2;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void merge_o_kernel(const T* o_a, const float* lse_a,
+                                                      const T* o_b, const float* lse_b,
+                                                      T* o_out, int64_t rowheads,
+                                                      int32_t head_dim) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const int64_t n = rowheads * head_dim;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rh = idx / head_dim;
+    const float la = lse_a[rh], lb = lse_b[rh];
+    const float mt = fmaxf(la, lb);
+    float out = 0.f;
+    if (mt != kNegInf) {
+      const float wa = fast_exp2((la - mt) * kLog2e);
+      const float wb = fast_exp2((lb - mt) * kLog2e);
+      // a side with no key carries weight 0 and must not poison the sum
+      const float ta = wa > 0.f ? wa * to_f32(o_a[idx]) : 0.f;
+      const float tb = wb > 0.f ? wb * to_f32(o_b[idx]) : 0.f;
+      out = (ta + tb) / (wa + wb);
+    }
+    o_out[idx] = from_f32<T>(out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// debug gather: logical K/V rows through the attention kernel's address path
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  constexpr int CH = D / 8;
+  const int b = blockIdx.y;
+  const ReqInfo rq = a.reqs[b];
+  const int j0 = blockIdx.x * 64;
+  if (j0 >= rq.kv_len) return;
+  const T* kp = static_cast<const T*>(a.k);
+  const T* vp = static_cast<const T*>(a.v);
+  T* ko = static_cast<T*>(a.k_out);
+  T* vo = static_cast<T*>(a.v_out);
+  const int total = 64 * a.num_kv_heads * CH;
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int part = idx % CH;
+    const int h = (idx / CH) % a.num_kv_heads;
+    const int j = j0 + idx / (CH * a.num_kv_heads);
+    if (j >= rq.kv_len) continue;
+    const int64_t ks = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift, a.k_s_page,
+                                 a.k_s_tok, a.k_s_head, h);
+    const int64_t vs = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift, a.v_s_page,
+                                 a.v_s_tok, a.v_s_head, h);
+    const int64_t dst = ((int64_t)(rq.kv_out_start + j) * a.num_kv_heads + h) * D + part * 8;
+    *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(kp + ks + part * 8);
+    *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(vp + vs + part * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
+  if (a.num_work == 0) return hipSuccess;
+  dim3 grid(a.num_work);
+  switch (tile_kind) {
+    case TILE_PREFILL:
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64>), grid, dim3(256), 0, s, a);
+      break;
+    case TILE_SHORT16:
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32>), grid, dim3(256), 0, s, a);
+      break;
+    case TILE_SHORT32:
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32>), grid, dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                            hipStream_t s) {
+  if (dtype == 1 && head_dim == 128) return launch_attention_t<__bf16, 128>(tile_kind, a, s);
+  if (dtype == 1 && head_dim == 64) return launch_attention_t<__bf16, 64>(tile_kind, a, s);
+  if (dtype == 0 && head_dim == 128) return launch_attention_t<_Float16, 128>(tile_kind, a, s);
+  if (dtype == 0 && head_dim == 64) return launch_attention_t<_Float16, 64>(tile_kind, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a, hipStream_t s) {
+  if (a.num_items == 0) return hipSuccess;
+  dim3 grid(a.num_items);
+  if (dtype == 1 && head_dim == 128)
+    hipLaunchKernelGGL((split_merge_kernel<__bf16, 128>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && head_dim == 64)
+    hipLaunchKernelGGL((split_merge_kernel<__bf16, 64>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 128)
+    hipLaunchKernelGGL((split_merge_kernel<_Float16, 128>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 64)
+    hipLaunchKernelGGL((split_merge_kernel<_Float16, 64>), grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_merge_t(const void* o_a, const float* lse_a, const void* o_b,
+                                 const float* lse_b, void* o_out, float* lse_out, int64_t rh,
+                                 int32_t d, hipStream_t s) {
+  const int64_t n = rh * d;
+  const int64_t blocks_o = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+  const int64_t blocks_l = (rh + 255) / 256 < 65536 ? (rh + 255) / 256 : 65536;
+  // o first (it reads the old lse), then lse: in-place merges stay correct.
+  hipLaunchKernelGGL((merge_o_kernel<T>), dim3((unsigned)blocks_o), dim3(256), 0, s,
+                     static_cast<const T*>(o_a), lse_a, static_cast<const T*>(o_b), lse_b,
+                     static_cast<T*>(o_out), rh, d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)blocks_l), dim3(256), 0, s, lse_a, lse_b,
+                     lse_out, rh);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a, const void* o_b,
+                               const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                               int32_t heads, int32_t head_dim, hipStream_t s) {
+  const int64_t rh = rows * heads;
+  if (rh == 0 || head_dim == 0) return hipSuccess;
+  if (dtype == 1)
+    return launch_merge_t<__bf16>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rh, head_dim, s);
+  if (dtype == 0)
+    return launch_merge_t<_Float16>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rh, head_dim, s);
+  if (dtype == 2)
+    return launch_merge_t<float>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rh, head_dim, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.max_kv_len == 0) return hipSuccess;
+  dim3 grid((a.max_kv_len + 63) / 64, a.batch);
+  if (dtype == 1 && head_dim == 128)
+    hipLaunchKernelGGL((gather_kernel<__bf16, 128>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && head_dim == 64)
+    hipLaunchKernelGGL((gather_kernel<__bf16, 64>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 128)
+    hipLaunchKernelGGL((gather_kernel<_Float16, 128>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 64)
+    hipLaunchKernelGGL((gather_kernel<_Float16, 64>), grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv

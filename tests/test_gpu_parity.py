@@ -1,0 +1,363 @@
+"""GPU parity: the HIP library against the float64 oracle on the same seeded inputs.
+
+Tolerances: max |do| <= 1e-2 (fp16) / 2e-2 (bf16), |dlse| <= 1e-3; page
+gathering is bit-exact.  Full-size workloads are checked on sampled
+(request, row, head) outputs computed one by one by the oracle.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import (assert_close, check_sampled, device_inputs, oracle_full, plan_for,
+                      require_gpu, run, to_device, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    return require_gpu()
+
+
+def _tiny(rng, qo_lens, kv_lens, hq, hkv, d, page, causal, w, dtype, poison=True, seed=0):
+    return W.build("tiny", qo_lens, kv_lens, hq, hkv, d, page, causal, w, dtype, seed=seed,
+                   poison=poison)
+
+
+# ---------------------------------------------------------------------------
+# config 1: single request, contiguous KV, fp16
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("window_left", [-1, 31])
+def test_config1_single_contiguous(pk, window_left):
+    results = []
+    for page_size in (16, 128):   # identity page table of 8 pages, or one page of 128
+        w = W.config1(window_left=window_left, page_size=page_size, poison=True)
+        assert list(w.kv_page_indices) == list(range(len(w.kv_page_indices)))
+        o, lse, _ = run(pk, w)
+        ref_o, ref_lse = oracle_full(w)
+        assert_close(o, lse, ref_o, ref_lse, w.dtype, f"config1 P={page_size} w={window_left}")
+        results.append((o, lse))
+    assert np.abs(results[0][0] - results[1][0]).max() <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# tiny exhaustive grid: pages, heads, masks, tiles, dtypes, head dims
+# ---------------------------------------------------------------------------
+GRID = []
+for d in (64, 128):
+    for dtype in (W.BF16, W.FP16):
+        for (hq, hkv) in ((1, 1), (4, 2), (6, 3), (8, 1)):
+            for page in (1, 3, 16):
+                GRID.append((d, dtype, hq, hkv, page))
+
+
+@pytest.mark.parametrize("d,dtype,hq,hkv,page", GRID)
+def test_tiny_grid(pk, d, dtype, hq, hkv, page):
+    rng = np.random.default_rng(zlib.crc32(repr((d, dtype, hq, hkv, page)).encode()))
+    B = int(rng.integers(1, 4))
+    qo = rng.integers(1, 40, size=B)
+    kv = qo + rng.integers(0, 150, size=B)
+    L = int(kv.max())
+    for causal in (True, False):
+        for w in sorted({-1, 0, 1, 7, L - 2, L - 1, L + 5}):
+            wl = _tiny(rng, qo, kv, hq, hkv, d, page, causal, w, dtype,
+                       seed=int(rng.integers(1 << 30)))
+            ref_o, ref_lse = oracle_full(wl)
+            tensors = device_inputs(wl)
+            for tile in (1, 2):
+                o, lse, _ = run(pk, wl, tensors, tile=tile)
+                assert_close(o, lse, ref_o, ref_lse, dtype,
+                             f"grid d={d} {dtype} h={hq}/{hkv} P={page} causal={causal} w={w} "
+                             f"tile={tile}")
+
+
+def test_ragged_tails_and_empty_requests(pk):
+    # requests with no query rows, one row, and lengths just past tile edges
+    qo = [0, 1, 33, 0, 129, 17]
+    kv = [5, 64, 65, 0, 129, 300]
+    for tile in (0, 1, 2):
+        w = W.build("ragged", qo, kv, 8, 2, 128, 16, True, -1, W.BF16, seed=7, poison=True)
+        o, lse, _ = run(pk, w, tile=tile)
+        ref_o, ref_lse = oracle_full(w)
+        assert_close(o, lse, ref_o, ref_lse, w.dtype, f"ragged tile={tile}")
+
+
+def test_empty_batch(pk):
+    p = pk.plan([0], [0], [], [], 4, 2, 64, 16, True, dtype=torch.float16)
+    q = torch.zeros((0, 4, 64), dtype=torch.float16, device="cuda")
+    k = torch.zeros((1, 16, 2, 64), dtype=torch.float16, device="cuda")
+    o, lse = p.run(q, k, k)
+    assert o.shape == (0, 4, 64) and lse.shape == (0, 4)
+
+
+# ---------------------------------------------------------------------------
+# config 2: paged batch prefill (full size, sampled outputs)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("window_left", [-1, 127])
+def test_config2_paged_prefill(pk, window_left):
+    w = W.config2(window_left=window_left, poison=True)
+    o, lse, p = run(pk, w)
+    assert p.info["tile_rows"] == 128
+    check_sampled(w, o, lse, np.random.default_rng(2), f"config2 w={window_left}")
+
+
+# ---------------------------------------------------------------------------
+# config 3: non-causal sliding window, page 1024 and 16
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("page_size", [1024, 16])
+def test_config3_noncausal_window(pk, page_size):
+    outs = {}
+    base = W.config3(window_left=0, page_size=page_size, poison=True)
+    floats = base.float_inputs()
+    tensors = device_inputs(base)
+    for wl in (0, 31, 127, 8192, -1):
+        w = base.with_window(wl)
+        o, lse, _ = run(pk, w, tensors)
+        outs[wl] = (o, lse)
+        if wl != -1:
+            check_sampled(w, o, lse, np.random.default_rng(3), f"config3 P={page_size} w={wl}",
+                          floats=floats)
+    # a window wider than the sequence is the unwindowed result, bit for bit
+    assert np.array_equal(outs[8192][0], outs[-1][0])
+    assert np.array_equal(outs[8192][1], outs[-1][1])
+    assert np.abs(outs[0][0] - outs[-1][0]).max() > 0.1   # non-vacuous
+
+
+# ---------------------------------------------------------------------------
+# config 4: speculative verify
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("batch", [4, 16, 64])
+@pytest.mark.parametrize("num_kv_heads", [4, 8])
+def test_config4_verify(pk, batch, num_kv_heads):
+    w = W.config4(batch=batch, num_kv_heads=num_kv_heads, poison=True)
+    q, k, v = device_inputs(w)
+    p = pk.verify_plan(w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 4, w.num_qo_heads,
+                       w.num_kv_heads, w.head_dim, w.page_size, dtype=torch.bfloat16)
+    o, lse = p.run(q, k, v)
+    # the verify wrapper is exactly a causal prefill over a stride-4 qo_indptr
+    o2, lse2, _ = run(pk, w, (q, k, v))
+    assert np.array_equal(o.float().cpu().numpy(), o2)
+    check_sampled(w, o2, lse2, np.random.default_rng(4), f"config4 B={batch} Hkv={num_kv_heads}",
+                  per_request=4 if batch <= 16 else 1, heads=4)
+
+
+# ---------------------------------------------------------------------------
+# config 5: long context, KV split into 8 chunks and merged
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("qo_len", [1, 64])
+@pytest.mark.parametrize("window_left", [-1, 4095])
+def test_config5_split_kv(pk, qo_len, window_left):
+    w = W.config5(qo_len=qo_len, window_left=window_left, poison=False)
+    floats = w.float_inputs()
+    tensors = device_inputs(w)
+    o8, lse8, p8 = run(pk, w, tensors, num_kv_chunks=W.CONFIG5_CHUNKS)
+    assert p8.info["num_merge_items"] > 0
+    check_sampled(w, o8, lse8, np.random.default_rng(5), f"config5 q={qo_len} w={window_left}",
+                  floats=floats, per_request=2, heads=3)
+    oa, lsea, _ = run(pk, w, tensors)   # scheduler's own split
+    assert np.abs(oa - o8).max() <= 2e-2
+    assert np.abs(lsea - lse8).max() <= 1e-3
+    # the same 8 chunks as separate partial states, folded with merge_states
+    q, k, v = tensors
+    chunk = 65536 // W.CONFIG5_CHUNKS
+    acc_o = acc_l = None
+    for c in range(W.CONFIG5_CHUNKS):
+        p = plan_for(pk, w, kv_begin=c * chunk, kv_end=(c + 1) * chunk)
+        po = torch.empty((w.total_q, w.num_qo_heads, w.head_dim), dtype=torch.float32,
+                         device="cuda")
+        pb, pl = p.run(q, k, v)
+        po.copy_(pb.float())
+        if acc_o is None:
+            acc_o, acc_l = po, pl
+        else:
+            acc_o, acc_l = pk.merge_states(acc_o, acc_l, po, pl)
+    torch.cuda.synchronize()
+    mo, ml = acc_o.cpu().numpy(), acc_l.cpu().numpy()
+    assert np.abs(mo - o8).max() <= 2e-2
+    assert np.abs(ml - lse8).max() <= 1e-3
+    check_sampled(w, mo, ml, np.random.default_rng(6), "config5 merge_states fold",
+                  floats=floats, per_request=2, heads=3)
+
+
+# ---------------------------------------------------------------------------
+# gather: bit-exact through the kernel's own page address path
+# ---------------------------------------------------------------------------
+def _np_gather(w, pool):
+    out = []
+    for b in range(w.batch_size):
+        L = int(w.kv_lens[b])
+        first = int(w.kv_indptr[b])
+        for j in range(L):
+            out.append(pool[w.kv_page_indices[first + j // w.page_size], j % w.page_size])
+    return np.stack(out) if out else np.zeros((0, w.num_kv_heads, w.head_dim), pool.dtype)
+
+
+@pytest.mark.parametrize("case", ["config2", "nonpow2", "hnd"])
+def test_gather_bit_exact(pk, case):
+    if case == "config2":
+        w = W.config2(poison=True)
+    else:
+        w = W.build("g", [3, 1, 7], [50, 7, 200], 8, 4, 64, 3 if case == "nonpow2" else 16,
+                    True, -1, W.FP16, seed=9, poison=True)
+    q, k, v = device_inputs(w)
+    p = plan_for(pk, w)
+    layout = "NHD"
+    if case == "hnd":   # same pool stored as [pages, heads, page_size, dim]
+        k = k.permute(0, 2, 1, 3).contiguous()
+        v = v.permute(0, 2, 1, 3).contiguous()
+        layout = "HND"
+    ko, vo = p.debug_gather(k, v, kv_layout=layout)
+    torch.cuda.synchronize()
+    view = np.int16 if w.dtype == W.BF16 else np.float16
+    got_k = ko.cpu().view(torch.int16 if w.dtype == W.BF16 else torch.float16).numpy()
+    got_v = vo.cpu().view(torch.int16 if w.dtype == W.BF16 else torch.float16).numpy()
+    want_k = _np_gather(w, w.k_pool).astype(view)
+    want_v = _np_gather(w, w.v_pool).astype(view)
+    assert np.array_equal(got_k.view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(got_v.view(np.uint16), want_v.view(np.uint16))
+    if case == "hnd":
+        o1, l1 = p.run(q, k, v, kv_layout="HND")
+        o2, l2 = p.run(*device_inputs(w))
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+def test_page_relabelling_bitwise(pk):
+    w = W.build("relabel", [40, 100], [300, 180], 8, 2, 128, 16, True, 50, W.BF16, seed=10)
+    o1, l1, _ = run(pk, w)
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(w.num_pages)
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    w2 = W.Workload(**{**w.__dict__, "kv_page_indices": perm[w.kv_page_indices].astype(np.int32),
+                       "k_pool": k2, "v_pool": v2})
+    o2, l2, _ = run(pk, w2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_closed_forms_on_gpu(pk):
+    # K = 0: lse_i = log(number of visible keys), o_i = mean of the visible V rows
+    w = W.build("kzero", [5, 64], [23, 200], 8, 2, 128, 16, True, 9, W.BF16, seed=12)
+    w.k_pool[:] = 0
+    o, lse, _ = run(pk, w)
+    ref_o, ref_lse = oracle_full(w)
+    assert_close(o, lse, ref_o, ref_lse, w.dtype, "K=0")
+    for b in range(2):
+        Q, L = int(w.qo_lens[b]), int(w.kv_lens[b])
+        for i in range(Q):
+            lo = max(0, L + i - Q - 9)
+            hi = i + L - Q
+            r = int(w.qo_indptr[b]) + i
+            assert np.abs(lse[r] - np.log(hi - lo + 1)).max() <= 1e-3
+    # V = 1: every softmax row sums to one
+    w = W.build("vone", [7, 33], [40, 90], 4, 4, 64, 3, False, 20, W.FP16, seed=13)
+    w.v_pool[:] = np.float16(1.0)
+    o, _, _ = run(pk, w)
+    assert np.abs(o - 1.0).max() <= 1e-2
+
+
+def test_gqa_equals_replicated_heads(pk):
+    w = W.build("gqa", [17, 30], [60, 33], 8, 2, 64, 16, True, -1, W.BF16, seed=14)
+    o1, l1, _ = run(pk, w)
+    rep = W.Workload(**{**w.__dict__, "num_kv_heads": 8,
+                        "k_pool": np.repeat(w.k_pool, 4, axis=2),
+                        "v_pool": np.repeat(w.v_pool, 4, axis=2)})
+    o2, l2, _ = run(pk, rep)
+    assert np.abs(o1 - o2).max() <= 2e-2 and np.abs(l1 - l2).max() <= 1e-3
+
+
+def test_split_equals_unsplit(pk):
+    w = W.build("split", [3, 70, 1], [5000, 3000, 900], 16, 4, 128, 16, True, -1, W.BF16,
+                seed=15, poison=True)
+    ref_o, ref_lse = oracle_full(w)
+    for chunks in (0, 1, 2, 3, 8):
+        for tile in (1, 2):
+            o, lse, p = run(pk, w, num_kv_chunks=chunks, tile=tile)
+            assert_close(o, lse, ref_o, ref_lse, w.dtype, f"chunks={chunks} tile={tile}")
+
+
+def test_key_range_partial_state(pk):
+    w = W.build("range", [6, 40], [100, 70], 4, 2, 128, 16, True, 10, W.BF16, seed=16)
+    for a, e in ((0, 30), (30, 64), (64, 101), (90, 95)):
+        o, lse, _ = run(pk, w, kv_begin=a, kv_end=e)
+        ref_o, ref_lse = oracle_full(w, kv_begin=a, kv_end=e)
+        assert_close(o, lse, ref_o, ref_lse, w.dtype, f"range [{a},{e})")
+
+
+# ---------------------------------------------------------------------------
+# merge_states
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_merge_states(pk, dtype):
+    rng = np.random.default_rng(17)
+    rows, heads, d = 37, 5, 96
+    oa = rng.standard_normal((rows, heads, d)).astype(np.float32)
+    ob = rng.standard_normal((rows, heads, d)).astype(np.float32)
+    la = (rng.standard_normal((rows, heads)) * 3).astype(np.float32)
+    lb = (rng.standard_normal((rows, heads)) * 3).astype(np.float32)
+    la[0, :] = -np.inf
+    lb[1, :] = -np.inf
+    la[2, :] = lb[2, :] = -np.inf
+    oa[0], ob[1] = 0, 0
+    ta, tb = torch.from_numpy(oa).to(dtype).cuda(), torch.from_numpy(ob).to(dtype).cuda()
+    tla, tlb = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
+    o, lse = pk.merge_states(ta, tla, tb, tlb)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.merge_states(ta.float().cpu().numpy(), la, tb.float().cpu().numpy(), lb)
+    tol = 1e-5 if dtype == torch.float32 else 2e-2
+    assert np.abs(o.float().cpu().numpy() - ref_o).max() <= tol
+    got_l = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.abs(got_l[fin] - ref_l[fin]).max() <= 1e-5
+    # a -inf side leaves the other state unchanged, exactly
+    assert torch.equal(o[1], ta[1]) and torch.equal(lse[1], tla[1])
+    # in place
+    o2, l2 = pk.merge_states(ta, tla, tb, tlb, out=ta, lse_out=tla)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(l2, lse)
+
+
+# ---------------------------------------------------------------------------
+# refusals at run time
+# ---------------------------------------------------------------------------
+def test_run_refuses_mismatches(pk):
+    w = W.build("refuse", [4, 9], [20, 30], 8, 2, 128, 16, True, -1, W.BF16, seed=18)
+    q, k, v = device_inputs(w)
+    p = plan_for(pk, w)
+
+    def refused(status, fn):
+        with pytest.raises(pk.PkvError) as e:
+            fn()
+        assert e.value.status_name == status, str(e.value)
+        return str(e.value)
+
+    msg = refused("EMISMATCH", lambda: p.run(q[:, :4], k, v))
+    assert "planned 8" in msg and "given 4" in msg
+    refused("EMISMATCH", lambda: p.run(q[:5], k, v))                       # too few rows
+    refused("EMISMATCH", lambda: p.run(q, k[:, :, :1], v))                 # kv heads
+    refused("EMISMATCH", lambda: p.run(q, k[:, :8], v[:, :8]))             # page size
+    refused("EMISMATCH", lambda: p.run(q.half(), k, v))                    # dtype
+    refused("EINVAL", lambda: p.run(q, k[:1], v[:1]))                      # pool too small
+    qs = torch.empty((q.shape[0], 8, 256), dtype=q.dtype, device=q.device)[:, :, ::2]
+    refused("ELAYOUT", lambda: p.run(qs, k, v))                            # strided head_dim
+    # padded q / o are accepted (token counts are minimums) and o rows past the plan untouched
+    qp = torch.zeros((q.shape[0] + 5, 8, 128), dtype=q.dtype, device=q.device)
+    qp[:q.shape[0]] = q
+    out = torch.full((q.shape[0] + 5, 8, 128), 7.0, dtype=q.dtype, device=q.device)
+    o, _ = p.run(qp, k, v, out=out)
+    o_ref, _ = p.run(q, k, v)
+    assert torch.equal(o[:q.shape[0]], o_ref) and torch.all(o[q.shape[0]:] == 7)
+    # a strided q (a slice of a fused qkv tensor) is honoured, not refused
+    qkv = torch.zeros((q.shape[0], 12, 128), dtype=q.dtype, device=q.device)
+    qkv[:, :8] = q
+    o_s, _ = p.run(qkv[:, :8], k, v)
+    assert torch.equal(o_s, o_ref)

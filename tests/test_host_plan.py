@@ -1,0 +1,188 @@
+"""Host logic of the C-ABI library, on the CPU (no device call is made):
+exported symbols, every plan refusal, and the scheduler's task list."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_prefill_amd as pk
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", header))
+    assert {"pkv_plan", "pkv_run", "pkv_merge_states", "pkv_workspace_size",
+            "pkv_plan_destroy", "pkv_last_error"} <= declared
+    lib = ctypes.CDLL(pk.library_path())
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in include/pkv.h but not exported"
+    pk.load_library()
+    assert b"gfx950" in pk.load_library().pkv_version()
+
+
+def _base():
+    return dict(qo_indptr=[0, 4, 10], kv_indptr=[0, 2, 5], kv_page_indices=[3, 0, 1, 4, 2],
+                kv_last_page_len=[5, 16], num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                page_size=16, causal=True, window_left=-1)
+
+
+def refused(status, **over):
+    args = {**_base(), **over}
+    with pytest.raises(pk.PkvError) as e:
+        pk.plan_host(**args)
+    assert e.value.status_name == status, str(e.value)
+    return str(e.value)
+
+
+def test_plan_refusals():
+    assert pk.plan_host(**_base()).info["num_work_items"] > 0
+    assert "given 12" in refused("EGQA", num_qo_heads=12, num_kv_heads=8)
+    refused("EGQA", num_qo_heads=4, num_kv_heads=8)
+    refused("EGQA", num_kv_heads=0)
+    refused("EGQA", num_kv_heads=-2)
+    refused("EINVAL", head_dim=96)
+    refused("EINVAL", page_size=0)
+    refused("EINVAL", window_left=-2)
+    refused("EINVAL", qo_indptr=[1, 4, 10])
+    refused("EINVAL", kv_indptr=[0, 3, 2], kv_page_indices=[0, 1, 2])
+    refused("EINVAL", qo_indptr=[0, 4, 3])
+    assert "kv_last_page_len[0]" in refused("EINVAL", kv_last_page_len=[0, 16])
+    refused("EINVAL", kv_last_page_len=[17, 16])
+    refused("EINVAL", kv_page_indices=[3, 0, -1, 4, 2])
+    # causal with kv_len < qo_len: request 0 has 21 keys, give it 30 rows
+    msg = refused("EINVAL", qo_indptr=[0, 30, 36])
+    assert "request 0" in msg and "kv_len" in msg
+    # the same shape is fine without the causal mask
+    pk.plan_host(**{**_base(), "qo_indptr": [0, 30, 36], "causal": False})
+    # query rows but no key
+    refused("EINVAL", kv_indptr=[0, 0, 5], kv_page_indices=[1, 4, 2, 0, 3], causal=False)
+    # batch 0 needs 0 rows; indptr / last length mismatch is caught by the binding
+    assert pk.plan_host([0], [0], [], [], 4, 2, 64, 16, True).info["num_work_items"] == 0
+    refused("EINVAL", kv_last_page_len=[5])
+    refused("EINVAL", tile=3)
+    refused("EINVAL", num_kv_chunks=-1)
+    refused("EINVAL", kv_begin=10, kv_end=5)
+
+
+def test_rejected_plan_leaves_earlier_plan_usable():
+    good = pk.plan_host(**_base())
+    before = good.work_items().copy()
+    with pytest.raises(pk.PkvError):
+        pk.plan_host(**{**_base(), "num_qo_heads": 12, "num_kv_heads": 8})
+    assert np.array_equal(good.work_items(), before)
+    assert good.info["has_device_copy"] == 0
+
+
+def test_host_plan_cannot_run():
+    p = pk.plan_host(**_base())
+    with pytest.raises(pk.PkvError) as e:
+        p.run(None, None, None)
+    assert e.value.status_name == "ENOTPLANNED"
+
+
+def _visible(i, Q, L, causal, w):
+    hi = i + L - Q if causal else L - 1
+    lo = 0 if (w == -1) else max(0, L + i - Q - w)
+    return lo, min(hi, L - 1)
+
+
+def check_coverage(w, **opts):
+    """Every packed row of every (request, kv head) is in exactly one row tile, and
+    the tile's chunks cover each row's visible keys exactly once."""
+    args = w.plan_args()
+    p = pk.plan_host(**args, **opts)
+    items = p.work_items()
+    info = p.info
+    G = w.num_qo_heads // w.num_kv_heads
+    NK = info["tile_keys"]
+    kb, ke = opts.get("kv_begin", 0), opts.get("kv_end", -1)
+    tiles = {}
+    for (b, kvh, row0, nrows, lo, end, slot, tb) in items:
+        assert tb % NK == 0 and tb <= max(lo, 0)
+        assert nrows <= info["tile_rows"]
+        tiles.setdefault((b, kvh, row0, nrows), []).append((lo, end, slot))
+    slots = [s for (_, _, _, _, _, _, s, _) in items if s >= 0]
+    assert sorted(slots) == list(range(info["num_partial_slots"]))
+    for b in range(w.batch_size):
+        Q, L = int(w.qo_lens[b]), int(w.kv_lens[b])
+        for kvh in range(w.num_kv_heads):
+            mine = sorted(t for t in tiles if t[0] == b and t[1] == kvh)
+            covered = []
+            for (_, _, row0, nrows) in mine:
+                covered.extend(range(row0, row0 + nrows))
+            assert covered == list(range(Q * G))
+            for key in mine:
+                chunks = sorted(tiles[key])
+                if len(chunks) > 1:
+                    assert all(s >= 0 for (_, _, s) in chunks)
+                for (a, e_, _), (a2, _, _) in zip(chunks, chunks[1:]):
+                    assert e_ <= a2   # disjoint
+                _, _, row0, nrows = key
+                for r in range(row0, row0 + nrows):
+                    lo, hi = _visible(r // G, Q, L, w.causal, w.window_left)
+                    lo, hi = max(lo, kb), min(hi, L - 1 if ke < 0 else min(hi, ke - 1))
+                    need = set(range(lo, hi + 1))
+                    got = set()
+                    for (a, e_, _) in chunks:
+                        got |= set(range(a, e_)) & need
+                    assert got == need, (b, kvh, r)
+    return p
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c2w", "c3", "c4", "c5", "c5q1w"])
+def test_schedule_covers_every_visible_key(cfg):
+    w = {"c1": lambda: W.config1(window_left=31, values=False),
+         "c2": lambda: W.config2(values=False),
+         "c2w": lambda: W.config2(window_left=127, values=False),
+         "c3": lambda: W.config3(window_left=31, values=False),
+         "c4": lambda: W.config4(batch=4, num_kv_heads=4, values=False),
+         "c5": lambda: W.config5(qo_len=64, values=False),
+         "c5q1w": lambda: W.config5(qo_len=1, window_left=4095, values=False)}[cfg]()
+    if cfg in ("c2", "c3", "c5"):
+        # full coverage check is O(rows * keys) in Python: shrink the big ones
+        w = W.build(w.name, np.minimum(w.qo_lens, 120), np.minimum(w.kv_lens, 900),
+                    w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, w.causal,
+                    w.window_left, w.dtype, seed=1, values=False)
+    check_coverage(w)
+    for opts in ({"num_kv_chunks": 3}, {"tile": 1}, {"tile": 2}, {"kv_begin": 33, "kv_end": 700},
+                 {"num_kv_chunks": 8, "tile": 2}):
+        check_coverage(w, **opts)
+
+
+def test_wide_window_schedules_like_no_window():
+    w = W.config2(values=False)
+    a = pk.plan_host(**{**w.plan_args(), "window_left": -1}).work_items()
+    b = pk.plan_host(**{**w.plan_args(), "window_left": 5000}).work_items()
+    assert np.array_equal(a, b)
+
+
+def test_window_skips_pages():
+    w = W.config3(window_left=0, page_size=16, values=False)
+    narrow = pk.plan_host(**w.plan_args()).work_items()
+    full = pk.plan_host(**{**w.plan_args(), "window_left": -1}).work_items()
+    loaded = lambda it: int(np.sum(it[:, 5] - it[:, 7]))
+    assert loaded(narrow) * 4 < loaded(full)
+
+
+def test_forced_chunks_for_long_context():
+    w = W.config5(qo_len=64, values=False)
+    p = pk.plan_host(**w.plan_args(), num_kv_chunks=8)
+    assert p.info["num_merge_items"] == p.info["num_work_items"] // 8
+    ends = sorted(set(p.work_items()[:, 5].tolist()))
+    assert ends[:7] == [8192 * c for c in range(1, 8)]
+    assert all(e > 7 * 8192 for e in ends[7:])
+
+
+def test_verify_plan_is_causal_stride_k():
+    w = W.config4(batch=16, num_kv_heads=8, values=False)
+    a = pk.plan_host(**w.plan_args()).work_items()
+    qo = np.arange(17) * 4
+    b = pk.plan_host(qo, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 32, 8, 128, 16,
+                     True).work_items()
+    assert np.array_equal(a, b)

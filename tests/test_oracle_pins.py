@@ -449,3 +449,24 @@ def test_pins_reject_planted_mistakes(name):
     elif name == "reversed_head_dim":
         assert fails(check_golden_attention, _transposed_pv)
         assert fails(check_sdpa, _transposed_pv, rng)
+
+
+def test_sampled_rows_match_full_oracle():
+    rng = np.random.default_rng(23)
+    prob = small_problem(rng, [6, 9], [30, 12], 6, 2, 8, 4)
+    for causal, w in [(True, -1), (True, 3), (False, 2)]:
+        full = oracle.attention(**prob, causal=causal, window_left=w, sm_scale=0.6)
+        for b, rows in ((0, [0, 5, 2]), (1, [8, 0])):
+            heads = [5, 0, 3]
+            o, lse = oracle.attention_rows(**prob, causal=causal, window_left=w, sm_scale=0.6,
+                                           b=b, rows=rows, heads=heads)
+            base = int(prob["qo_indptr"][b])
+            for ri, i in enumerate(rows):
+                for hi, h in enumerate(heads):
+                    np.testing.assert_allclose(o[ri, hi], full[0][base + i, h], atol=1e-12)
+                    assert lse[ri, hi] == pytest.approx(full[1][base + i, h], abs=1e-12)
+    # restricted key range matches the full oracle's partial state
+    part = oracle.attention(**prob, causal=True, window_left=-1, sm_scale=0.6, kv_begin=4, kv_end=9)
+    o, lse = oracle.attention_rows(**prob, causal=True, window_left=-1, sm_scale=0.6, b=1,
+                                   rows=[0, 8], heads=[1], kv_begin=4, kv_end=9)
+    np.testing.assert_allclose(o[:, 0], part[0][[6, 14], 1], atol=1e-12)
