@@ -1,0 +1,209 @@
+"""Benchmark: paged-KV attention prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--secondary]
+
+One step = plan (host validation + scheduling + one async copy) and run
+(attention + split merge) over the paged batch-prefill workload: batch 8,
+qo ~ U[128, 1024], kv = qo + U[0, 2048], page 16 in a permuted pool 1.5x the
+pages needed, Hq 32 / Hkv 8, head_dim 128, bf16, causal.  Inputs are resident
+in HBM before the timed region.  value = algorithmic TFLOP/s over the whole
+step (4 * head_dim flops per visible (query, key) pair per q head).
+
+Prints ONE JSON line.  `roofline` covers the attention kernel: its average
+duration comes from HIP events around each launch on the stream it runs on.
+`cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
+workload (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "masked-attention TFLOP/s (prefill) + KV HBM GB/s (verify), fraction of peak"
+
+
+def visible_pairs(w):
+    """Number of (row, key) pairs the mask keeps, per q head, summed over requests."""
+    total = 0
+    for b in range(w.batch_size):
+        Q, L = int(w.qo_lens[b]), int(w.kv_lens[b])
+        i = np.arange(Q, dtype=np.int64)
+        hi = i + L - Q if w.causal else np.full(Q, L - 1)
+        hi = np.minimum(hi, L - 1)
+        lo = np.zeros(Q, dtype=np.int64) if w.window_left < 0 else np.maximum(0, L + i - Q - w.window_left)
+        total += int(np.maximum(hi - lo + 1, 0).sum())
+    return total
+
+
+def attention_flops(w):
+    return 4.0 * w.head_dim * w.num_qo_heads * visible_pairs(w)
+
+
+def kv_bytes(w):
+    """K and V rows any row of a request can see, x Hkv x 2 x D x 2 bytes, plus q, o, lse."""
+    elem = 2
+    keys = 0
+    for b in range(w.batch_size):
+        Q, L = int(w.qo_lens[b]), int(w.kv_lens[b])
+        hi = L - 1
+        lo = 0 if w.window_left < 0 else max(0, L - Q - w.window_left)
+        keys += hi - lo + 1
+    kv = keys * w.num_kv_heads * 2 * w.head_dim * elem
+    qo = 2 * w.total_q * w.num_qo_heads * w.head_dim * elem + w.total_q * w.num_qo_heads * 4
+    return kv + qo
+
+
+def _device_inputs(w, dev):
+    import torch
+    view = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+    conv = (lambda a: torch.from_numpy(a).view(view).to(dev)) if w.dtype == W.BF16 else \
+        (lambda a: torch.from_numpy(a).to(dev))
+    return conv(w.q), conv(w.k_pool), conv(w.v_pool)
+
+
+def time_kernel(pk, p, tensors, iters):
+    """Average run() duration from HIP events on the launch stream (ms)."""
+    import torch
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    q, k, v = tensors
+    o = torch.empty((p.total_q_rows, p.num_qo_heads, p.head_dim), dtype=p.dtype, device=q.device)
+    lse = torch.empty((p.total_q_rows, p.num_qo_heads), dtype=torch.float32, device=q.device)
+    for a, b in evs:
+        a.record(s)
+        p.run(q, k, v, out=o, lse=lse)
+        b.record(s)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The float64 oracle on requests of the workload, until ~budget_s of work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    qf, kf, vf = w.float_inputs()
+    order = np.argsort(w.qo_lens * w.kv_lens)   # cheapest requests first
+    done, flops, t0 = [], 0.0, time.perf_counter()
+    for b in order:
+        sub = W.Workload(**{**w.__dict__,
+                            "qo_lens": w.qo_lens[b:b + 1], "kv_lens": w.kv_lens[b:b + 1],
+                            "qo_indptr": np.array([0, w.qo_lens[b]], np.int32),
+                            "kv_indptr": np.array([0, w.kv_indptr[b + 1] - w.kv_indptr[b]], np.int32),
+                            "kv_page_indices": w.kv_page_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]],
+                            "kv_last_page_len": w.kv_last_page_len[b:b + 1]})
+        q0, q1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        a = sub.plan_args()
+        del a["head_dim"]
+        oracle.attention(qf[q0:q1], kf, vf, **a)
+        done.append(int(b))
+        flops += attention_flops(sub)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle over {len(done)} of {w.batch_size} requests "
+                      f"(indices {sorted(done)}), all {w.num_qo_heads} q heads, {dt:.1f} s; "
+                      f"host has {os.cpu_count()} logical CPUs"}
+
+
+def secondary_verify(pk, torch, dev, batch=64, hkv=8, iters=20):
+    """Speculative verify: KV GB/s of run() on the verify workload."""
+    w = W.config4(batch=batch, num_kv_heads=hkv)
+    tensors = _device_inputs(w, dev)
+    p = pk.verify_plan(w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 4, w.num_qo_heads,
+                       w.num_kv_heads, w.head_dim, w.page_size, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        p.run(*tensors)
+    ms = time_kernel(pk, p, tensors, iters)
+    nbytes = kv_bytes(w)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+            "bytes": nbytes, "work_items": p.info["num_work_items"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--window-left", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", action="store_true", help="also time speculative verify")
+    ap.add_argument("--kernel-iters", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-KV prefill path has no multi-GPU "
+              "component here (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_prefill_amd as pk
+    pk.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = W.config2(window_left=args.window_left)
+    tensors = _device_inputs(w, dev)
+    plan_args = w.plan_args()
+    flops = attention_flops(w)
+
+    def step():
+        p = pk.plan(**plan_args, dtype=torch.bfloat16, device=dev)
+        p.run(*tensors)
+        return p
+
+    for _ in range(args.warmup):
+        p = step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        p = step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / args.steps * 1e3
+    value = flops / (dt / args.steps) / 1e12
+
+    kernel_ms = time_kernel(pk, p, tensors, args.kernel_iters)
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch_size,
+                   "qo_len": "U[128,1024]", "kv_len": "qo + U[0,2048]", "page_size": w.page_size,
+                   "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "causal": w.causal, "window_left": w.window_left,
+                   "total_q": w.total_q, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attn_kernel (prefill tile)", "kernel_ms": kernel_ms},
+    }
+    if args.secondary:
+        result["secondary"] = {"verify": secondary_verify(pk, torch, dev)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
