@@ -75,7 +75,8 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python -m paged_kv_cache_prefill_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
+    # resolve every symbol now: a missing kernel stub must fail here, not mid-run
+    lib = ctypes.CDLL(_LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     pi32 = ctypes.POINTER(ctypes.c_int32)
     lib.pkv_last_error.restype = ctypes.c_char_p

@@ -79,47 +79,69 @@ __device__ __forceinline__ T from_f32(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Element offset of (page-table slot of key j, head h, element 0) in a pool.
-__device__ __forceinline__ int64_t kv_offset(const int32_t* pages, int32_t page_off, int32_t j,
-                                             int32_t page_size, int32_t page_shift,
-                                             int64_t s_page, int64_t s_tok, int64_t s_head,
-                                             int32_t h) {
-  int32_t pidx, slot;
-  if (page_shift >= 0) {
-    pidx = j >> page_shift;
-    slot = j & (page_size - 1);
-  } else {
-    pidx = j / page_size;
-    slot = j - pidx * page_size;
-  }
-  const int64_t page = pages[page_off + pidx];
+// Page-table address path shared by the attention and debug-gather kernels:
+// logical key j of a request lives on page pages[page_off + j / P] at slot j % P.
+__device__ __forceinline__ int32_t page_of(const int32_t* pages, int32_t page_off, int32_t j,
+                                           int32_t page_size, int32_t page_shift) {
+  const int32_t pidx = page_shift >= 0 ? (j >> page_shift) : (j / page_size);
+  return pages[page_off + pidx];
+}
+__device__ __forceinline__ int32_t slot_of(int32_t j, int32_t page_size, int32_t page_shift) {
+  return page_shift >= 0 ? (j & (page_size - 1)) : (j % page_size);
+}
+// Element offset of (page, slot, head h, element 0) in a pool.
+__device__ __forceinline__ int64_t row_offset(int64_t page, int32_t slot, int64_t s_page,
+                                              int64_t s_tok, int64_t s_head, int32_t h) {
   return page * s_page + (int64_t)slot * s_tok + (int64_t)h * s_head;
 }
 
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
+// LDS tiles hold key rows of D elements as 16-byte chunks, row-major and
+// unpadded; chunk c of row r sits at position c ^ (r & 7).  The XOR spreads
+// the rows that one MFMA fragment read touches over all 32 banks, both for
+// the K reads (16 rows x 4 chunks) and for the transposing V reads.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 16 bytes from global memory straight into LDS: lane i of the wave writes
+// dst + 16 * i (dst is wave-uniform).
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+// Wait for every outstanding memory operation of this wave.
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Two transposing 8-byte LDS reads joined into one 8-element fragment.
+__device__ __forceinline__ i16x8 lds_read_tr16_x2(const char* p0, const char* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // WM waves split the rows, WN waves split the keys of each LDS tile;
 // each wave owns QB blocks of 16 rows and NW keys of the tile.
 template <typename T, int D, int WM, int WN, int QB, int NW>
 __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
   using Tr = Traits<T>;
   using frag = typename Tr::frag;
-  constexpr int NT = 64 * WM * WN;
-  constexpr int MW = 16 * QB;    // rows per wave
-  constexpr int NWG = NW * WN;   // keys per LDS tile
-  constexpr int CH = D / 8;      // 16-byte chunks per key row
-  constexpr int RP = CH + 1;     // LDS row pitch in chunks (one chunk of padding)
-  constexpr int NL = NWG * CH / NT;  // chunks each thread loads per tile (per K and V)
-  constexpr int DK = D / 32;     // MFMA k-steps over head_dim
-  constexpr int KB = NW / 16;    // 16-key blocks per wave
-  constexpr int DB = D / 16;     // 16-wide head_dim blocks of the output
-  static_assert(NWG * CH % NT == 0, "tile not divisible among threads");
-  static_assert(NW % 32 == 0, "wave key tile must be a multiple of 32");
+  constexpr int NWAVE = WM * WN;
+  constexpr int MW = 16 * QB;           // rows per wave
+  constexpr int NWG = NW * WN;          // keys per LDS tile
+  constexpr int CH = D / 8;             // 16-byte chunks per key row
+  constexpr int TCH = NWG * CH;         // chunks per tile (K or V)
+  constexpr int NI = TCH / (64 * NWAVE);  // direct-load instructions per wave per tile
+  constexpr int RPI = 64 / CH;          // key rows filled by one wave instruction
+  constexpr int DK = D / 32;            // MFMA k-steps over head_dim
+  constexpr int KB = NW / 16;           // 16-key blocks per wave
+  constexpr int DB = D / 16;            // 16-wide head_dim blocks of the output
+  static_assert(TCH % (64 * NWAVE) == 0, "tile not divisible among waves");
+  static_assert(NW % 32 == 0 && CH >= 8, "shape");
 
-  __shared__ uint4 smem[2 * 2 * NWG * RP];
-  uint4* lds_k = smem;                 // [2][NWG][RP]
-  uint4* lds_v = smem + 2 * NWG * RP;  // [2][NWG][RP]
+  __shared__ uint4 smem[2 * 2 * TCH];   // [buf][K, V][TCH]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,8 +154,8 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
   const WorkItem it = a.work[blockIdx.x];
   const ReqInfo rq = a.reqs[it.b];
   const int G = a.group;
-  const int R = rq.qo_len * G;          // packed rows of this (request, kv head)
-  const int shift_q = rq.kv_len - rq.qo_len;  // bottom-right offset L - Q
+  const int R = rq.qo_len * G;                  // packed rows of this (request, kv head)
+  const int shift_q = rq.kv_len - rq.qo_len;    // bottom-right offset L - Q
   const int win = rq.window;
 
   const T* __restrict__ qp = static_cast<const T*>(a.q);
@@ -152,13 +174,11 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
       const int h = it.kvh * G + (r - pos * G);
       const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
 #pragma unroll
-      for (int dk = 0; dk < DK; ++dk) {
-        uint4 u = *reinterpret_cast<const uint4*>(src + dk * 32 + g * 8);
-        qf[qb][dk] = __builtin_bit_cast(frag, u);
-      }
+      for (int dk = 0; dk < DK; ++dk)
+        qf[qb][dk] = __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(src + dk * 32 + g * 8));
       int l0 = 0;
       if (win >= 0) l0 = max(0, pos + shift_q - win);
-      int h0 = a.causal ? pos + shift_q : rq.kv_len - 1;
+      const int h0 = a.causal ? pos + shift_q : rq.kv_len - 1;
       lo[qb] = max(l0, it.key_lo);
       hi[qb] = min(h0, it.kv_end - 1);
     } else {
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // Range of keys every valid row of the task sees (tiles inside it need no mask).
+  // Keys every valid row of the task sees: tiles inside need no mask.
   int full_lo, full_hi;
   {
     const int rmax = min(it.row0 + it.nrows, R) - 1;
@@ -181,7 +201,6 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
     full_hi = min(full_hi, it.kv_end - 1);
   }
 
-  // ---- accumulators
   f32x4 oacc[DB][QB];
   float m_run[QB], l_run[QB];
 #pragma unroll
@@ -193,49 +212,56 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
   }
 
   const int ntiles = it.kv_end > it.tile_begin ? (it.kv_end - it.tile_begin + NWG - 1) / NWG : 0;
+  const int last_key = it.kv_end - 1;
 
-  uint4 kreg[NL], vreg[NL];
-  auto load_tile = [&](int j0) {
+  // Direct global->LDS loads: wave instruction m fills tile slots
+  // [(m * NWAVE + wave) * 64, +64); lane i writes slot +i, which is key row
+  // (m * NWAVE + wave) * RPI + i / CH at position i % CH, i.e. logical chunk
+  // (i % CH) ^ (row & 7).  Keys at or past kv_end read the last key instead
+  // (finite data, masked to zero weight), so no read leaves the request.
+  int pid_next[NI];
+  auto fetch_pids = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < NL; ++r) {
-      const int c = tid + r * NT;
-      const int key = c / CH;
-      const int part = c - key * CH;
-      const int j = j0 + key;
-      if (j < it.kv_end) {
-        const int64_t ko = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift,
-                                     a.k_s_page, a.k_s_tok, a.k_s_head, it.kvh);
-        const int64_t vo = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift,
-                                     a.v_s_page, a.v_s_tok, a.v_s_head, it.kvh);
-        kreg[r] = *reinterpret_cast<const uint4*>(kp + ko + part * 8);
-        vreg[r] = *reinterpret_cast<const uint4*>(vp + vo + part * 8);
-      } else {
-        kreg[r] = make_uint4(0, 0, 0, 0);
-        vreg[r] = make_uint4(0, 0, 0, 0);
-      }
+    for (int m = 0; m < NI; ++m) {
+      const int row = (m * NWAVE + wave) * RPI + lane / CH;
+      const int j = min(j0 + row, last_key);
+      pid_next[m] = page_of(a.pages, rq.page_off, j, a.page_size, a.page_shift);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto issue_tile = [&](int j0, int buf) {
+    uint4* kdst = smem + (buf * 2 + 0) * TCH;
+    uint4* vdst = smem + (buf * 2 + 1) * TCH;
 #pragma unroll
-    for (int r = 0; r < NL; ++r) {
-      const int c = tid + r * NT;
-      const int key = c / CH;
-      const int part = c - key * CH;
-      lds_k[(buf * NWG + key) * RP + part] = kreg[r];
-      lds_v[(buf * NWG + key) * RP + part] = vreg[r];
+    for (int m = 0; m < NI; ++m) {
+      const int row = (m * NWAVE + wave) * RPI + lane / CH;
+      const int j = min(j0 + row, last_key);
+      const int slot = slot_of(j, a.page_size, a.page_shift);
+      const int c = swz(row, lane % CH);
+      const int64_t ko = row_offset(pid_next[m], slot, a.k_s_page, a.k_s_tok, a.k_s_head, it.kvh) + c * 8;
+      const int64_t vo = row_offset(pid_next[m], slot, a.v_s_page, a.v_s_tok, a.v_s_head, it.kvh) + c * 8;
+      const int base = (m * NWAVE + wave) * 64;
+      load_lds16(kp + ko, kdst + base);
+      load_lds16(vp + vo, vdst + base);
     }
   };
 
   if (ntiles > 0) {
-    load_tile(it.tile_begin);
-    store_tile(0);
+    fetch_pids(it.tile_begin);
+    issue_tile(it.tile_begin, 0);
+    if (ntiles > 1) fetch_pids(it.tile_begin + NWG);
   }
+  wait_all();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = it.tile_begin + t * NWG;
     const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(j0 + NWG);
+    if (t + 1 < ntiles) {
+      issue_tile(j0 + NWG, buf ^ 1);
+      if (t + 2 < ntiles) fetch_pids(j0 + 2 * NWG);
+    }
+    const uint4* kt = smem + (buf * 2 + 0) * TCH;
+    const char* vt = reinterpret_cast<const char*>(smem + (buf * 2 + 1) * TCH);
 
     // ---- S^T = K Q^T for this wave's NW keys
     f32x4 s[KB][QB];
@@ -243,19 +269,19 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint4* kt = lds_k + (buf * NWG + wn * NW) * RP;
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const frag af = __builtin_bit_cast(frag, kt[(kb * 16 + l16) * RP + dk * 4 + g]);
+        const int row = wn * NW + kb * 16 + l16;
+        const frag af = __builtin_bit_cast(frag, kt[row * CH + swz(row, dk * 4 + g)]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(af, qf[qb][dk], s[kb][qb]);
       }
     }
 
-    // ---- scale, mask, online softmax (lane owns row l16 of each qb block,
-    // keys kb*16 + 4*g + i)
+    // ---- mask (partial tiles only) and online softmax; lane owns row l16 of
+    // each qb block and keys kb*16 + 4g + i of the wave's slice
     const int jw = j0 + wn * NW;
     const bool full = (j0 >= full_lo) && (j0 + NWG - 1 <= full_hi);
 #pragma unroll
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[kb][qb][i] * a.scale_log2;
+          float x = s[kb][qb][i];
           if (!full) {
             const int j = jw + kb * 16 + 4 * g + i;
             if (j < lo[qb] || j > hi[qb]) x = kNegInf;
@@ -276,7 +302,7 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx);
+      const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[qb] - m_use);
       m_run[qb] = m_new;
@@ -285,20 +311,24 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(s[kb][qb][i] - m_use);
+          const float p = fast_exp2(__builtin_fmaf(s[kb][qb][i], a.scale_log2, -m_use));
           s[kb][qb][i] = p;
           rs += p;
         }
       }
       l_run[qb] = l_run[qb] * alpha + rs;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+      }
     }
 
     // ---- O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
-    // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, which is
-    // exactly where S^T put them; the A operand reads the same keys of V.
-    const T* vt = reinterpret_cast<const T*>(lds_v + (buf * NWG + wn * NW) * RP);
+    // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
+    // S^T left them.  The A operand (V^T) comes from two transposing LDS
+    // reads: lane r of each 16-lane group points at 4 head-dim elements
+    // d0 + 4(r%4) of key 4g + r/4 (+16); the read hands lane t element
+    // V[4g + k][d0 + t] as its element k.
 #pragma unroll
     for (int st = 0; st < NW / 32; ++st) {
       frag pb[QB];
@@ -310,21 +340,21 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
           pb[qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
         }
       }
+      const int key0 = wn * NW + st * 32 + 4 * g + (l16 >> 2);
+      const int key1 = key0 + 16;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        frag af;
-        const int d = db * 16 + l16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = st * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-          af[e] = vt[key * RP * 8 + d];
-        }
+        const int d = db * 16 + 4 * (l16 & 3);        // first of 4 elements this lane points at
+        const int c = d >> 3, off = (d & 7) * 2;      // chunk and byte offset inside it
+        const int a0 = (key0 * CH + swz(key0, c)) * 16 + off;
+        const int a1 = (key1 * CH + swz(key1, c)) * 16 + off;
+        const frag af = __builtin_bit_cast(frag, lds_read_tr16_x2(vt + a0, vt + a1));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(af, pb[qb], oacc[db][qb]);
       }
     }
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    wait_all();
     __syncthreads();
   }
 
@@ -402,7 +432,7 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     // Every thread finishes 4 consecutive head-dim elements of some rows.
-    for (int idx = tid; idx < MW * (D / 4); idx += NT) {
+    for (int idx = tid; idx < MW * (D / 4); idx += 64 * NWAVE) {
       const int rl = idx / (D / 4);
       const int d4 = idx - rl * (D / 4);
       float mt = kNegInf;
@@ -542,10 +572,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int h = (idx / CH) % a.num_kv_heads;
     const int j = j0 + idx / (CH * a.num_kv_heads);
     if (j >= rq.kv_len) continue;
-    const int64_t ks = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift, a.k_s_page,
-                                 a.k_s_tok, a.k_s_head, h);
-    const int64_t vs = kv_offset(a.pages, rq.page_off, j, a.page_size, a.page_shift, a.v_s_page,
-                                 a.v_s_tok, a.v_s_head, h);
+    const int32_t page = page_of(a.pages, rq.page_off, j, a.page_size, a.page_shift);
+    const int32_t slot = slot_of(j, a.page_size, a.page_shift);
+    const int64_t ks = row_offset(page, slot, a.k_s_page, a.k_s_tok, a.k_s_head, h);
+    const int64_t vs = row_offset(page, slot, a.v_s_page, a.v_s_tok, a.v_s_head, h);
     const int64_t dst = ((int64_t)(rq.kv_out_start + j) * a.num_kv_heads + h) * D + part * 8;
     *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(kp + ks + part * 8);
     *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(vp + vs + part * 8);

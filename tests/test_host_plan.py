@@ -19,7 +19,7 @@ def test_library_exports_every_declared_symbol():
     declared = set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", header))
     assert {"pkv_plan", "pkv_run", "pkv_merge_states", "pkv_workspace_size",
             "pkv_plan_destroy", "pkv_last_error"} <= declared
-    lib = ctypes.CDLL(pk.library_path())
+    lib = ctypes.CDLL(pk.library_path(), mode=os.RTLD_NOW)   # every symbol resolvable
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} declared in include/pkv.h but not exported"
     pk.load_library()
