@@ -377,7 +377,7 @@ struct pkv_plan_s {
   Schedule S;
   pkv_dtype dtype;
   float sm_scale;
-  int32_t page_shift;
+  uint32_t page_magic = 1, page_shift = 0;
   uint8_t* int_ws = nullptr;
   float* float_ws = nullptr;
   bool has_device_copy = false;
@@ -431,12 +431,7 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
   const Schedule& S = p->S;
   p->dtype = dtype;
   p->sm_scale = sm_scale;
-  p->page_shift = -1;
-  if ((page_size & (page_size - 1)) == 0) {
-    int sh = 0;
-    while ((1 << sh) < page_size) ++sh;
-    p->page_shift = sh;
-  }
+  page_divider((uint32_t)page_size, &p->page_magic, &p->page_shift);
   const bool dry = (int_ws == nullptr && int_ws_bytes == 0);
   if (!dry) {
     if (!int_ws || int_ws_bytes < S.int_bytes) {
@@ -545,6 +540,13 @@ pkv_status check_cache(const pkv_plan_s* p, const char* name, const void* ptr, i
                 "%s strides (page %lld, token %lld, head %lld): expected non-negative multiples "
                 "of 8 elements with a packed head_dim",
                 name, (long long)s_page, (long long)s_tok, (long long)s_head);
+  // the kernels address a key as page * s_page (64-bit) + an in-page offset (32-bit)
+  const int64_t in_page = (int64_t)(psize - 1) * s_tok + (int64_t)(heads - 1) * s_head + dim;
+  if (s_page >= (1ll << 31) || in_page >= (1ll << 31))
+    return fail(PKV_ELAYOUT,
+                "%s strides (page %lld, token %lld, head %lld): one page must span fewer than "
+                "2^31 elements",
+                name, (long long)s_page, (long long)s_tok, (long long)s_head);
   return PKV_OK;
 }
 
@@ -615,16 +617,17 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
                            : nullptr;
   a.q_s_tok = q_s_tok;
   a.q_s_head = q_s_head;
-  a.k_s_page = k_s_page;
-  a.k_s_tok = k_s_tok;
-  a.k_s_head = k_s_head;
-  a.v_s_page = v_s_page;
-  a.v_s_tok = v_s_tok;
-  a.v_s_head = v_s_head;
+  a.k_s_page = (uint32_t)k_s_page;
+  a.k_s_tok = (uint32_t)k_s_tok;
+  a.k_s_head = (uint32_t)k_s_head;
+  a.v_s_page = (uint32_t)v_s_page;
+  a.v_s_tok = (uint32_t)v_s_tok;
+  a.v_s_head = (uint32_t)v_s_head;
   a.num_work = (int32_t)S.work.size();
   a.group = S.group;
   a.num_qo_heads = S.hq;
   a.page_size = S.page_size;
+  a.page_magic = p->page_magic;
   a.page_shift = p->page_shift;
   a.causal = S.causal;
   a.scale_log2 = p->sm_scale * 1.4426950408889634f;
@@ -700,14 +703,15 @@ pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_
   g.v_out = v_out;
   g.pages = reinterpret_cast<const int32_t*>(p->int_ws + S.off_pages);
   g.reqs = reinterpret_cast<const ReqInfo*>(p->int_ws + S.off_reqs);
-  g.k_s_page = k_s_page;
-  g.k_s_tok = k_s_tok;
-  g.k_s_head = k_s_head;
-  g.v_s_page = v_s_page;
-  g.v_s_tok = v_s_tok;
-  g.v_s_head = v_s_head;
+  g.k_s_page = (uint32_t)k_s_page;
+  g.k_s_tok = (uint32_t)k_s_tok;
+  g.k_s_head = (uint32_t)k_s_head;
+  g.v_s_page = (uint32_t)v_s_page;
+  g.v_s_tok = (uint32_t)v_s_tok;
+  g.v_s_head = (uint32_t)v_s_head;
   g.num_kv_heads = S.hkv;
   g.page_size = S.page_size;
+  g.page_magic = p->page_magic;
   g.page_shift = p->page_shift;
   g.max_kv_len = S.max_kv_len;
   g.batch = S.batch;

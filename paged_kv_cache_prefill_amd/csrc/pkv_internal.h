@@ -45,6 +45,22 @@ inline int tile_rows(int kind) {
 }
 inline int tile_keys(int kind) { return kind == TILE_PREFILL ? 64 : 128; }
 
+// Multiply-shift constants for j / page_size over 0 <= j < 2^31: a power of
+// two 2^l uses (1, l); otherwise m = floor(2^(31+l) / P) + 1 with
+// l = ceil(log2 P) and shift 31 + l (round-up reciprocal; the error
+// j * (m - 2^(31+l)/P) / 2^(31+l) stays below 1/P, so the floor is exact).
+inline void page_divider(uint32_t page_size, uint32_t* magic, uint32_t* shift) {
+  uint32_t l = 0;
+  while ((1ull << l) < page_size) ++l;
+  if ((1u << l) == page_size) {
+    *magic = 1;
+    *shift = l;
+  } else {
+    *magic = (uint32_t)(((1ull << (31 + l)) / page_size) + 1);
+    *shift = 31 + l;
+  }
+}
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -57,13 +73,17 @@ struct AttnArgs {
   float* part_o;           // [slots][tile_rows][head_dim] fp32
   float* part_lse;         // [slots][tile_rows] fp32, log2 domain
   int64_t q_s_tok, q_s_head;
-  int64_t k_s_page, k_s_tok, k_s_head;
-  int64_t v_s_page, v_s_tok, v_s_head;
+  // pool strides in elements; the host guarantees that every in-page offset
+  // (slot * s_tok + head * s_head + head_dim) fits in 31 bits
+  uint32_t k_s_page, k_s_tok, k_s_head;
+  uint32_t v_s_page, v_s_tok, v_s_head;
   int32_t num_work;
   int32_t group;           // num_qo_heads / num_kv_heads
   int32_t num_qo_heads;
   int32_t page_size;
-  int32_t page_shift;      // log2(page_size) or -1
+  // page index of key j: (j * page_magic) >> page_shift, exact for 0 <= j < 2^31
+  uint32_t page_magic;
+  uint32_t page_shift;
   int32_t causal;
   float scale_log2;        // sm_scale * log2(e)
 };
@@ -88,11 +108,12 @@ struct GatherArgs {
   void* v_out;
   const int32_t* pages;
   const ReqInfo* reqs;
-  int64_t k_s_page, k_s_tok, k_s_head;
-  int64_t v_s_page, v_s_tok, v_s_head;
+  uint32_t k_s_page, k_s_tok, k_s_head;
+  uint32_t v_s_page, v_s_tok, v_s_head;
   int32_t num_kv_heads;
   int32_t page_size;
-  int32_t page_shift;
+  uint32_t page_magic;
+  uint32_t page_shift;
   int32_t max_kv_len;
   int32_t batch;
 };

@@ -79,20 +79,21 @@ __device__ __forceinline__ T from_f32(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Page-table address path shared by the attention and debug-gather kernels:
-// logical key j of a request lives on page pages[page_off + j / P] at slot j % P.
-__device__ __forceinline__ int32_t page_of(const int32_t* pages, int32_t page_off, int32_t j,
-                                           int32_t page_size, int32_t page_shift) {
-  const int32_t pidx = page_shift >= 0 ? (j >> page_shift) : (j / page_size);
-  return pages[page_off + pidx];
+
+// Page-table address path, shared by the attention and debug-gather kernels:
+// logical key j of a request lives on page ptab[j / P] at slot j % P, and
+// element e of head h of that key at page * s_page + slot * s_tok + h * s_head + e.
+struct KeyLoc {
+  uint32_t page, slot;
+};
+__device__ __forceinline__ KeyLoc locate_key(const int32_t* ptab, uint32_t j, uint32_t magic,
+                                             uint32_t shift, uint32_t page_size) {
+  const uint32_t pidx = (uint32_t)(((uint64_t)j * magic) >> shift);
+  return KeyLoc{(uint32_t)ptab[pidx], j - pidx * page_size};
 }
-__device__ __forceinline__ int32_t slot_of(int32_t j, int32_t page_size, int32_t page_shift) {
-  return page_shift >= 0 ? (j & (page_size - 1)) : (j % page_size);
-}
-// Element offset of (page, slot, head h, element 0) in a pool.
-__device__ __forceinline__ int64_t row_offset(int64_t page, int32_t slot, int64_t s_page,
-                                              int64_t s_tok, int64_t s_head, int32_t h) {
-  return page * s_page + (int64_t)slot * s_tok + (int64_t)h * s_head;
+__device__ __forceinline__ uint64_t key_offset(KeyLoc k, uint32_t s_page, uint32_t s_tok,
+                                               uint32_t in_page) {
+  return (uint64_t)k.page * s_page + (k.slot * s_tok + in_page);
 }
 
 // ---------------------------------------------------------------------------
@@ -121,11 +122,18 @@ __device__ __forceinline__ i16x8 lds_read_tr16_x2(const char* p0, const char* p1
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+__device__ __forceinline__ bool wave_any(bool x) { return __any(x); }
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 // WM waves split the rows, WN waves split the keys of each LDS tile;
-// each wave owns QB blocks of 16 rows and NW keys of the tile.
-template <typename T, int D, int WM, int WN, int QB, int NW>
-__global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
+// each wave owns QB blocks of 16 rows and NW keys of the tile.  WPE is the
+// number of waves per SIMD the register budget is sized for.
+template <typename T, int D, int WM, int WN, int QB, int NW, int WPE>
+__global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   using Tr = Traits<T>;
   using frag = typename Tr::frag;
   constexpr int NWAVE = WM * WN;
@@ -219,51 +227,39 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
   // (m * NWAVE + wave) * RPI + i / CH at position i % CH, i.e. logical chunk
   // (i % CH) ^ (row & 7).  Keys at or past kv_end read the last key instead
   // (finite data, masked to zero weight), so no read leaves the request.
-  int pid_next[NI];
-  auto fetch_pids = [&](int j0) {
+  uint32_t koff[NI], voff[NI];   // in-page element offsets of this lane's chunks
+  int lrow[NI];
 #pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      const int row = (m * NWAVE + wave) * RPI + lane / CH;
-      const int j = min(j0 + row, last_key);
-      pid_next[m] = page_of(a.pages, rq.page_off, j, a.page_size, a.page_shift);
-    }
+  for (int m = 0; m < NI; ++m) {
+    lrow[m] = (m * NWAVE + wave) * RPI + lane / CH;
+    const uint32_t c8 = (uint32_t)swz(lrow[m], lane % CH) * 8;
+    koff[m] = c8 + (uint32_t)it.kvh * a.k_s_head;
+    voff[m] = c8 + (uint32_t)it.kvh * a.v_s_head;
+  }
+  KeyLoc loc[NI];
+  const int32_t* ptab = a.pages + rq.page_off;
+  auto fetch_pages = [&](int j0) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m)
+      loc[m] = locate_key(ptab, (uint32_t)min(j0 + lrow[m], last_key), a.page_magic,
+                          a.page_shift, (uint32_t)a.page_size);
   };
-  auto issue_tile = [&](int j0, int buf) {
+  auto issue_tile = [&](int buf) {
     uint4* kdst = smem + (buf * 2 + 0) * TCH;
     uint4* vdst = smem + (buf * 2 + 1) * TCH;
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
-      const int row = (m * NWAVE + wave) * RPI + lane / CH;
-      const int j = min(j0 + row, last_key);
-      const int slot = slot_of(j, a.page_size, a.page_shift);
-      const int c = swz(row, lane % CH);
-      const int64_t ko = row_offset(pid_next[m], slot, a.k_s_page, a.k_s_tok, a.k_s_head, it.kvh) + c * 8;
-      const int64_t vo = row_offset(pid_next[m], slot, a.v_s_page, a.v_s_tok, a.v_s_head, it.kvh) + c * 8;
+      const uint64_t ko = key_offset(loc[m], a.k_s_page, a.k_s_tok, koff[m]);
+      const uint64_t vo = key_offset(loc[m], a.v_s_page, a.v_s_tok, voff[m]);
       const int base = (m * NWAVE + wave) * 64;
       load_lds16(kp + ko, kdst + base);
       load_lds16(vp + vo, vdst + base);
     }
   };
 
-  if (ntiles > 0) {
-    fetch_pids(it.tile_begin);
-    issue_tile(it.tile_begin, 0);
-    if (ntiles > 1) fetch_pids(it.tile_begin + NWG);
-  }
-  wait_all();
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = it.tile_begin + t * NWG;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      issue_tile(j0 + NWG, buf ^ 1);
-      if (t + 2 < ntiles) fetch_pids(j0 + 2 * NWG);
-    }
-    const uint4* kt = smem + (buf * 2 + 0) * TCH;
-    const char* vt = reinterpret_cast<const char*>(smem + (buf * 2 + 1) * TCH);
-
-    // ---- S^T = K Q^T for this wave's NW keys
+  // One LDS tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](auto masked, const uint4* kt, const char* vt, int j0) {
+    constexpr bool MASKED = decltype(masked)::value;
     f32x4 s[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -280,10 +276,8 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
       }
     }
 
-    // ---- mask (partial tiles only) and online softmax; lane owns row l16 of
-    // each qb block and keys kb*16 + 4g + i of the wave's slice
-    const int jw = j0 + wn * NW;
-    const bool full = (j0 >= full_lo) && (j0 + NWG - 1 <= full_hi);
+    // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
+    const int jl = j0 + wn * NW + 4 * g;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = kNegInf;
@@ -292,11 +286,11 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = s[kb][qb][i];
-          if (!full) {
-            const int j = jw + kb * 16 + 4 * g + i;
-            if (j < lo[qb] || j > hi[qb]) x = kNegInf;
+          if constexpr (MASKED) {
+            const int j = jl + kb * 16 + i;
+            x = (j >= lo[qb] && j <= hi[qb]) ? x : kNegInf;
+            s[kb][qb][i] = x;
           }
-          s[kb][qb][i] = x;
           mx = fmaxf(mx, x);
         }
       }
@@ -317,13 +311,13 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
         }
       }
       l_run[qb] = l_run[qb] * alpha + rs;
-      if (__any(alpha != 1.f)) {
+      if (wave_any(alpha != 1.f)) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
       }
     }
 
-    // ---- O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
+    // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
     // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
     // S^T left them.  The A operand (V^T) comes from two transposing LDS
     // reads: lane r of each 16-lane group points at 4 head-dim elements
@@ -353,7 +347,29 @@ __global__ __launch_bounds__(64 * WM * WN) void attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(af, pb[qb], oacc[db][qb]);
       }
     }
+  };
 
+  if (ntiles > 0) {
+    fetch_pages(it.tile_begin);
+    issue_tile(0);
+    if (ntiles > 1) fetch_pages(it.tile_begin + NWG);
+  }
+  wait_all();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = it.tile_begin + t * NWG;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      issue_tile(buf ^ 1);
+      if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
+    }
+    const uint4* kt = smem + (buf * 2 + 0) * TCH;
+    const char* vt = reinterpret_cast<const char*>(smem + (buf * 2 + 1) * TCH);
+    if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
+      tile(Flag<false>{}, kt, vt, j0);
+    else
+      tile(Flag<true>{}, kt, vt, j0);
     wait_all();
     __syncthreads();
   }
@@ -572,10 +588,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int h = (idx / CH) % a.num_kv_heads;
     const int j = j0 + idx / (CH * a.num_kv_heads);
     if (j >= rq.kv_len) continue;
-    const int32_t page = page_of(a.pages, rq.page_off, j, a.page_size, a.page_shift);
-    const int32_t slot = slot_of(j, a.page_size, a.page_shift);
-    const int64_t ks = row_offset(page, slot, a.k_s_page, a.k_s_tok, a.k_s_head, h);
-    const int64_t vs = row_offset(page, slot, a.v_s_page, a.v_s_tok, a.v_s_head, h);
+    const KeyLoc loc = locate_key(a.pages + rq.page_off, (uint32_t)j, a.page_magic, a.page_shift,
+                                  (uint32_t)a.page_size);
+    const uint64_t ks = key_offset(loc, a.k_s_page, a.k_s_tok, (uint32_t)h * a.k_s_head);
+    const uint64_t vs = key_offset(loc, a.v_s_page, a.v_s_tok, (uint32_t)h * a.v_s_head);
     const int64_t dst = ((int64_t)(rq.kv_out_start + j) * a.num_kv_heads + h) * D + part * 8;
     *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(kp + ks + part * 8);
     *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(vp + vs + part * 8);
@@ -591,13 +607,13 @@ static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream
   dim3 grid(a.num_work);
   switch (tile_kind) {
     case TILE_PREFILL:
-      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64, 2>), grid, dim3(256), 0, s, a);
       break;
     case TILE_SHORT16:
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32, 2>), grid, dim3(256), 0, s, a);
       break;
     case TILE_SHORT32:
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32, 2>), grid, dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;
