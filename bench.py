@@ -149,7 +149,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true", help="also time speculative verify")
     ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for profilers: 3 steps, 1 warmup, no baselines")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 256 MiB read + 256 MiB write elementwise kernel "
+                         "(scale for the HBM byte counters)")
     args = ap.parse_args()
+    if args.profile:
+        args.steps, args.warmup, args.kernel_iters = 3, 1, 3
+        args.no_cpu_baseline, args.secondary = True, False
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-KV prefill path has no multi-GPU "
               "component here (run with --gpus 1)", file=sys.stderr)
@@ -160,6 +168,13 @@ def main():
     pk.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calib_copy:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 2.0, out=dst)       # 256 MiB read, 256 MiB written
+        torch.cuda.synchronize()
+        del src, dst
 
     w = W.config2(window_left=args.window_left)
     tensors = _device_inputs(w, dev)

@@ -133,6 +133,9 @@ def _dtype_code(dtype):
 def _host_i32(x, name):
     if x is None:
         return None
+    if isinstance(x, np.ndarray) and x.dtype == np.int32 and x.ndim == 1 and \
+            x.flags.c_contiguous:
+        return x
     if hasattr(x, "detach"):  # torch tensor
         if x.is_cuda:
             raise PkvError(PKV_EINVAL, f"{name}: expected a host array, given a device tensor")

@@ -81,6 +81,84 @@ struct RowTask {
   int32_t tile_begin;
 };
 
+// Work-group i of a launch runs on XCD i % 8, and each XCD has its own L2.
+// Tasks of one (request, kv head) read the same K/V rows, so when there are
+// enough such groups they are bin-packed onto XCDs (largest group first, to
+// the least loaded XCD) and each XCD's list is interleaved into slots x,
+// x + 8, x + 16, ...; lists are padded with empty tasks (num_rows 0).  Within
+// an XCD, and in the fallback with too few groups, tasks run longest first
+// (a stable counting sort on the tile count), so the tail of the launch is
+// made of short tasks.
+constexpr int kNumXcds = 8;
+
+void sort_longest_first(const std::vector<WorkItem>& items, const std::vector<int32_t>& costs,
+                        const std::vector<int32_t>& idx, std::vector<WorkItem>* out) {
+  int32_t max_cost = 0;
+  for (int32_t i : idx) max_cost = std::max(max_cost, costs[i]);
+  std::vector<int32_t> start(max_cost + 2, 0);
+  for (int32_t i : idx) ++start[max_cost - costs[i] + 1];
+  for (int32_t c = 1; c <= max_cost + 1; ++c) start[c] += start[c - 1];
+  out->assign(idx.size(), WorkItem{});
+  for (int32_t i : idx) (*out)[start[max_cost - costs[i]]++] = items[i];
+}
+
+void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_t>& costs,
+                    int32_t hkv, std::vector<WorkItem>* work) {
+  const size_t n = items.size();
+  std::vector<int32_t> all(n);
+  std::iota(all.begin(), all.end(), 0);
+  // group costs, keyed by request * hkv + kv head
+  std::vector<int64_t> gcost;
+  std::vector<int32_t> gid(n);
+  int64_t total = 0;
+  for (size_t i = 0; i < n; ++i) {
+    gid[i] = items[i].b * hkv + items[i].kvh;
+    if ((size_t)gid[i] >= gcost.size()) gcost.resize(gid[i] + 1, 0);
+    gcost[gid[i]] += costs[i];
+    total += costs[i];
+  }
+  int64_t groups = 0, gmax = 0;
+  for (int64_t c : gcost) {
+    groups += c > 0;
+    gmax = std::max(gmax, c);
+  }
+  // Reuse exists only when a group has several query tiles (chunks of one
+  // tile read disjoint keys).  Tasks of one tile are emitted consecutively.
+  bool reuse = false;
+  for (size_t i = 1; i < n && !reuse; ++i)
+    reuse = gid[i] == gid[i - 1] && items[i].row0 != items[i - 1].row0;
+  if (!reuse || groups < 2 * kNumXcds || gmax * kNumXcds > total + total / 2) {
+    sort_longest_first(items, costs, all, work);
+    return;
+  }
+  std::vector<int32_t> gorder(gcost.size());
+  std::iota(gorder.begin(), gorder.end(), 0);
+  std::stable_sort(gorder.begin(), gorder.end(),
+                   [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
+  std::vector<int32_t> gxcd(gcost.size(), 0);
+  int64_t load[kNumXcds] = {0};
+  for (int32_t g : gorder) {
+    int best = 0;
+    for (int x = 1; x < kNumXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    gxcd[g] = best;
+    load[best] += gcost[g];
+  }
+  std::vector<int32_t> idx[kNumXcds];
+  for (size_t i = 0; i < n; ++i) idx[gxcd[gid[i]]].push_back((int32_t)i);
+  std::vector<WorkItem> lists[kNumXcds];
+  size_t longest = 0;
+  for (int x = 0; x < kNumXcds; ++x) {
+    sort_longest_first(items, costs, idx[x], &lists[x]);
+    longest = std::max(longest, lists[x].size());
+  }
+  WorkItem empty{};  // num_rows 0: the kernel returns at once
+  empty.slot = -1;
+  work->assign(longest * kNumXcds, empty);
+  for (int x = 0; x < kNumXcds; ++x)
+    for (size_t k = 0; k < lists[x].size(); ++k) (*work)[k * kNumXcds + x] = lists[x][k];
+}
+
 pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
                     const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
                     int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t page_size,
@@ -198,6 +276,11 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
   // ---- row tasks with their visible key ranges
   std::vector<RowTask> tasks;
+  {
+    int64_t n = 0;
+    for (int32_t b = 0; b < batch; ++b) n += ((int64_t)S->reqs[b].qo_len * G + MR - 1) / MR;
+    tasks.reserve((size_t)(n * hkv));
+  }
   for (int32_t b = 0; b < batch; ++b) {
     const ReqInfo& r = S->reqs[b];
     const int32_t R = r.qo_len * G;
@@ -235,7 +318,12 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     chunk_tiles = std::max<int64_t>(min_tiles, (total + kTargetTasks - 1) / kTargetTasks);
   }
 
-  std::vector<std::pair<int64_t, WorkItem>> items;  // (cost, item)
+  std::vector<WorkItem> items;
+  std::vector<int32_t> costs;
+  items.reserve(tasks.size() * 2);
+  costs.reserve(tasks.size() * 2);
+  std::vector<std::pair<int32_t, int32_t>> chunks;  // [c0, c1) key ranges of one task
+  chunks.reserve(64);
   auto emit = [&](const RowTask& t, int32_t lo, int32_t end, int32_t tb, int32_t slot) {
     WorkItem w;
     w.b = t.b;
@@ -246,8 +334,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     w.kv_end = end;
     w.slot = slot;
     w.tile_begin = tb;
-    const int64_t c = end > tb ? (end - tb + NK - 1) / NK : 0;
-    items.emplace_back(c, w);
+    items.push_back(w);
+    costs.push_back(end > tb ? (end - tb + NK - 1) / NK : 0);
   };
   int32_t slots = 0;
   for (const RowTask& t : tasks) {
@@ -255,7 +343,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
       emit(t, 0, 0, 0, -1);
       continue;
     }
-    std::vector<std::pair<int32_t, int32_t>> chunks;  // [c0, c1) key ranges
+    chunks.clear();
     if (o.num_kv_chunks > 0) {
       const int64_t L = S->reqs[t.b].kv_len;
       int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
@@ -294,16 +382,9 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     }
   }
   S->num_slots = slots;
-  // Longest tasks first so the tail of the launch is made of short ones.
-  std::stable_sort(items.begin(), items.end(),
-                   [](const std::pair<int64_t, WorkItem>& x, const std::pair<int64_t, WorkItem>& y) {
-                     return x.first > y.first;
-                   });
-  S->work.clear();
-  S->work.reserve(items.size());
-  for (const auto& it : items) S->work.push_back(it.second);
-  if (S->work.size() > (size_t)INT32_MAX / 2)
-    return fail(PKV_EINVAL, "batch too large: %zu tasks", S->work.size());
+  if (items.size() > (size_t)INT32_MAX / 2)
+    return fail(PKV_EINVAL, "batch too large: %zu tasks", items.size());
+  order_for_xcds(items, costs, hkv, &S->work);
 
   // ---- workspace layouts
   size_t off = 0;

@@ -45,6 +45,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kTau = 8.f;   // lazy-rescale threshold, log2 units
 constexpr float kNegInf = -__builtin_inff();
 
 template <typename T>
@@ -99,11 +100,22 @@ __device__ __forceinline__ uint64_t key_offset(KeyLoc k, uint32_t s_page, uint32
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
-// LDS tiles hold key rows of D elements as 16-byte chunks, row-major and
-// unpadded; chunk c of row r sits at position c ^ (r & 7).  The XOR spreads
-// the rows that one MFMA fragment read touches over all 32 banks, both for
-// the K reads (16 rows x 4 chunks) and for the transposing V reads.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS tiles hold key rows of D elements as CH = D/8 16-byte chunks,
+// row-major and unpadded, with the chunk order permuted per row so that the
+// reads of one MFMA fragment spread over all banks:
+//  * K (16-byte reads, consecutive lanes on consecutive rows, same chunk):
+//    chunk c of row r sits at position c ^ (r & 15) (r & 7 when CH = 8);
+//  * V (transposing 8-byte reads: 16 lanes cover 4 consecutive keys x 2
+//    adjacent chunks): chunk c of key k sits at c ^ ((2k) & (CH - 1)), which
+//    keeps those 8 chunks, and 32 lanes' 16, on distinct positions.
+template <int CH>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+  return chunk ^ (row & (CH >= 16 ? 15 : 7));
+}
+template <int CH>
+__device__ __forceinline__ int swz_v(int key, int chunk) {
+  return chunk ^ ((2 * key) & (CH - 1));
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -131,8 +143,12 @@ struct Flag {
 
 // WM waves split the rows, WN waves split the keys of each LDS tile;
 // each wave owns QB blocks of 16 rows and NW keys of the tile.  WPE is the
-// number of waves per SIMD the register budget is sized for.
-template <typename T, int D, int WM, int WN, int QB, int NW, int WPE>
+// number of waves per SIMD the register budget is sized for.  PM selects the
+// page addressing of complete key tiles: 0 any page size (per-key page-table
+// lookup), 1 power-of-two pages no longer than the tile (each lane's slot is
+// fixed), 2 power-of-two pages at least as long as the tile (one page per
+// tile).  The last, partial tile of a task always takes the general path.
+template <typename T, int D, int WM, int WN, int QB, int NW, int WPE, int PM>
 __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   using Tr = Traits<T>;
   using frag = typename Tr::frag;
@@ -149,17 +165,22 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   static_assert(TCH % (64 * NWAVE) == 0, "tile not divisible among waves");
   static_assert(NW % 32 == 0 && CH >= 8, "shape");
 
-  __shared__ uint4 smem[2 * 2 * TCH];   // [buf][K, V][TCH]
+  // Two K/V buffers as four separate LDS objects: the loop below is unrolled
+  // by two so every access names one fixed buffer, which lets the compiler
+  // see that the direct loads into one buffer cannot alias reads of the other
+  // (it then keeps those loads in flight across the tile's compute).
+  __shared__ uint4 lds_k0[TCH], lds_v0[TCH], lds_k1[TCH], lds_v1[TCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int wm = wave % WM;
   const int wn = wave / WM;
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
   const WorkItem it = a.work[blockIdx.x];
+  if (it.nrows == 0) return;                    // padding task (whole work group)
   const ReqInfo rq = a.reqs[it.b];
   const int G = a.group;
   const int R = rq.qo_len * G;                  // packed rows of this (request, kv head)
@@ -227,33 +248,58 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // (m * NWAVE + wave) * RPI + i / CH at position i % CH, i.e. logical chunk
   // (i % CH) ^ (row & 7).  Keys at or past kv_end read the last key instead
   // (finite data, masked to zero weight), so no read leaves the request.
-  uint32_t koff[NI], voff[NI];   // in-page element offsets of this lane's chunks
+  uint32_t koff[NI], voff[NI];   // element offsets of this lane's chunks within a key row
+  uint32_t kin[NI], vin[NI];     // ... plus the lane's fixed slot (PM 1) or row (PM 2)
   int lrow[NI];
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
     lrow[m] = (m * NWAVE + wave) * RPI + lane / CH;
-    const uint32_t c8 = (uint32_t)swz(lrow[m], lane % CH) * 8;
-    koff[m] = c8 + (uint32_t)it.kvh * a.k_s_head;
-    voff[m] = c8 + (uint32_t)it.kvh * a.v_s_head;
+    koff[m] = (uint32_t)swz_k<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.k_s_head;
+    voff[m] = (uint32_t)swz_v<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.v_s_head;
+    const uint32_t lslot = (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
+    kin[m] = lslot * a.k_s_tok + koff[m];
+    vin[m] = lslot * a.v_s_tok + voff[m];
   }
-  KeyLoc loc[NI];
+  KeyLoc loc[NI];           // page (and slot, general path) of each lane row of the next tile
+  uint32_t tile_page = 0;   // PM 2: the next tile's single page
   const int32_t* ptab = a.pages + rq.page_off;
   auto fetch_pages = [&](int j0) {
+    const bool fast = PM != 0 && j0 + NWG <= it.kv_end;
+    if (PM == 1 && fast) {
+      const int32_t* pt = ptab + (j0 >> a.page_shift);
 #pragma unroll
-    for (int m = 0; m < NI; ++m)
-      loc[m] = locate_key(ptab, (uint32_t)min(j0 + lrow[m], last_key), a.page_magic,
-                          a.page_shift, (uint32_t)a.page_size);
+      for (int m = 0; m < NI; ++m) loc[m].page = (uint32_t)pt[lrow[m] >> a.page_shift];
+    } else if (PM == 2 && fast) {
+      tile_page = (uint32_t)ptab[j0 >> a.page_shift];
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m)
+        loc[m] = locate_key(ptab, (uint32_t)min(j0 + lrow[m], last_key), a.page_magic,
+                            a.page_shift, (uint32_t)a.page_size);
+    }
   };
-  auto issue_tile = [&](int buf) {
-    uint4* kdst = smem + (buf * 2 + 0) * TCH;
-    uint4* vdst = smem + (buf * 2 + 1) * TCH;
+  auto issue_tile = [&](int j0, uint4* kdst, uint4* vdst) {
+    if (PM != 0 && j0 + NWG <= it.kv_end) {
+      const uint32_t slot0 = (uint32_t)j0 & (uint32_t)(a.page_size - 1);
+      const uint64_t kt0 = (uint64_t)tile_page * a.k_s_page + slot0 * a.k_s_tok;
+      const uint64_t vt0 = (uint64_t)tile_page * a.v_s_page + slot0 * a.v_s_tok;
 #pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      const uint64_t ko = key_offset(loc[m], a.k_s_page, a.k_s_tok, koff[m]);
-      const uint64_t vo = key_offset(loc[m], a.v_s_page, a.v_s_tok, voff[m]);
-      const int base = (m * NWAVE + wave) * 64;
-      load_lds16(kp + ko, kdst + base);
-      load_lds16(vp + vo, vdst + base);
+      for (int m = 0; m < NI; ++m) {
+        const uint64_t ko = PM == 1 ? (uint64_t)loc[m].page * a.k_s_page + kin[m] : kt0 + kin[m];
+        const uint64_t vo = PM == 1 ? (uint64_t)loc[m].page * a.v_s_page + vin[m] : vt0 + vin[m];
+        const int base = (m * NWAVE + wave) * 64;
+        load_lds16(kp + ko, kdst + base);
+        load_lds16(vp + vo, vdst + base);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const uint64_t ko = key_offset(loc[m], a.k_s_page, a.k_s_tok, koff[m]);
+        const uint64_t vo = key_offset(loc[m], a.v_s_page, a.v_s_tok, voff[m]);
+        const int base = (m * NWAVE + wave) * 64;
+        load_lds16(kp + ko, kdst + base);
+        load_lds16(vp + vo, vdst + base);
+      }
     }
   };
 
@@ -270,7 +316,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int row = wn * NW + kb * 16 + l16;
-        const frag af = __builtin_bit_cast(frag, kt[row * CH + swz(row, dk * 4 + g)]);
+        const frag af = __builtin_bit_cast(frag, kt[row * CH + swz_k<CH>(row, dk * 4 + g)]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(af, qf[qb][dk], s[kb][qb]);
       }
@@ -296,10 +342,20 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[qb] - m_use);
-      m_run[qb] = m_new;
+      // Lazy rescaling: exponents are taken against a reference m_run that
+      // only moves when some row of the wave sees a score more than kTau
+      // (log2 units) above it, so every p stays <= 2^kTau.  The reference
+      // cancels in o = sum p v / sum p and is added back into lse.
+      const float mxs = mx * a.scale_log2;
+      if (wave_any(mxs > m_run[qb] + kTau)) {
+        const float m_new = fmaxf(m_run[qb], mxs);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+      }
+      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -310,11 +366,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           rs += p;
         }
       }
-      l_run[qb] = l_run[qb] * alpha + rs;
-      if (wave_any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
-      }
+      l_run[qb] += rs;
     }
 
     // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
@@ -340,8 +392,8 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       for (int db = 0; db < DB; ++db) {
         const int d = db * 16 + 4 * (l16 & 3);        // first of 4 elements this lane points at
         const int c = d >> 3, off = (d & 7) * 2;      // chunk and byte offset inside it
-        const int a0 = (key0 * CH + swz(key0, c)) * 16 + off;
-        const int a1 = (key1 * CH + swz(key1, c)) * 16 + off;
+        const int a0 = (key0 * CH + swz_v<CH>(key0, c)) * 16 + off;
+        const int a1 = (key1 * CH + swz_v<CH>(key1, c)) * 16 + off;
         const frag af = __builtin_bit_cast(frag, lds_read_tr16_x2(vt + a0, vt + a1));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(af, pb[qb], oacc[db][qb]);
@@ -349,27 +401,39 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
   };
 
+  auto run_tile = [&](const uint4* kt, const uint4* vt, int j0) {
+    const char* vtc = reinterpret_cast<const char*>(vt);
+    if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
+      tile(Flag<false>{}, kt, vtc, j0);
+    else
+      tile(Flag<true>{}, kt, vtc, j0);
+  };
+
   if (ntiles > 0) {
     fetch_pages(it.tile_begin);
-    issue_tile(0);
+    issue_tile(it.tile_begin, lds_k0, lds_v0);
     if (ntiles > 1) fetch_pages(it.tile_begin + NWG);
   }
   wait_all();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = 0; t < ntiles; t += 2) {
     const int j0 = it.tile_begin + t * NWG;
-    const int buf = t & 1;
+    // even tile: compute from buffer 0 while buffer 1 fills
     if (t + 1 < ntiles) {
-      issue_tile(buf ^ 1);
+      issue_tile(j0 + NWG, lds_k1, lds_v1);
       if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
     }
-    const uint4* kt = smem + (buf * 2 + 0) * TCH;
-    const char* vt = reinterpret_cast<const char*>(smem + (buf * 2 + 1) * TCH);
-    if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
-      tile(Flag<false>{}, kt, vt, j0);
-    else
-      tile(Flag<true>{}, kt, vt, j0);
+    run_tile(lds_k0, lds_v0, j0);
+    wait_all();
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    // odd tile: compute from buffer 1 while buffer 0 fills
+    if (t + 2 < ntiles) {
+      issue_tile(j0 + 2 * NWG, lds_k0, lds_v0);
+      if (t + 3 < ntiles) fetch_pages(j0 + 3 * NWG);
+    }
+    run_tile(lds_k1, lds_v1, j0 + NWG);
     wait_all();
     __syncthreads();
   }
@@ -420,10 +484,15 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   } else {
     // Waves along keys hold partial states of the same rows: combine in LDS.
     static_assert(WM == 1, "key-split tiles use one row block");
-    float* red_m = reinterpret_cast<float*>(smem);       // [WN][MW]
+    // per-wave [MW][D] fp32 slices: waves 0..WN/2-1 in lds_k0, the rest in lds_k1
+    auto red_o_of = [&](int w) -> float* {
+      float* base = reinterpret_cast<float*>(w < WN / 2 ? lds_k0 : lds_k1);
+      return base + (w % (WN / 2)) * MW * D;
+    };
+    float* red_m = reinterpret_cast<float*>(lds_v0);     // [WN][MW]
     float* red_l = red_m + WN * MW;                      // [WN][MW]
-    float* red_o = red_l + WN * MW;                      // [WN][MW][D]
-    static_assert((2 * WN * MW + WN * MW * D) * 4 <= (int)sizeof(smem), "LDS too small");
+    static_assert(WN % 2 == 0 && (WN / 2) * MW * D * 4 <= (int)sizeof(lds_k0), "LDS too small");
+    static_assert(2 * WN * MW * 4 <= (int)sizeof(lds_v0), "LDS too small");
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (g == 0) {
@@ -443,7 +512,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 v = oacc[db][qb] * sc;
-        *reinterpret_cast<f32x4*>(red_o + ((wn * MW) + rl) * D + db * 16 + 4 * g) = v;
+        *reinterpret_cast<f32x4*>(red_o_of(wn) + rl * D + db * 16 + 4 * g) = v;
       }
     }
     __syncthreads();
@@ -460,7 +529,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < WN; ++w) {
         lt += red_l[w * MW + rl] * fast_exp2(red_m[w * MW + rl] - mu);
-        acc += *reinterpret_cast<const f32x4*>(red_o + (w * MW + rl) * D + d4 * 4);
+        acc += *reinterpret_cast<const f32x4*>(red_o_of(w) + rl * D + d4 * 4);
       }
       const int r = it.row0 + rl;
       if (rl >= it.nrows || r >= R) continue;
@@ -601,24 +670,33 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
-  if (a.num_work == 0) return hipSuccess;
+template <typename T, int D, int PM>
+static hipError_t launch_attention_pm(int tile_kind, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.num_work);
   switch (tile_kind) {
     case TILE_PREFILL:
-      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64, 2>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64, 2, PM>), grid, dim3(256), 0, s, a);
       break;
     case TILE_SHORT16:
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32, 2>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32, 2, PM>), grid, dim3(256), 0, s, a);
       break;
     case TILE_SHORT32:
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32, 2>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32, 2, PM>), grid, dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
+  if (a.num_work == 0) return hipSuccess;
+  const int nwg = tile_keys(tile_kind);
+  const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
+  if (pow2 && a.page_size <= nwg) return launch_attention_pm<T, D, 1>(tile_kind, a, s);
+  if (pow2) return launch_attention_pm<T, D, 2>(tile_kind, a, s);
+  return launch_attention_pm<T, D, 0>(tile_kind, a, s);
 }
 
 hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
