@@ -17,6 +17,7 @@ workload (rank 0, N = 1 only).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +34,28 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "masked-attention TFLOP/s (prefill) + KV HBM GB/s (verify), fraction of peak"
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_prefill_amd", "csrc", "pkv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_paged_b8_hbm.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the prefill attention kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy-kernel
+    calibration), or None when absent or taken on a different kernel source."""
+    try:
+        rec = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    rec[k.strip()] = v.strip()
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def visible_pairs(w):
@@ -125,13 +148,13 @@ def cpu_baseline(w, budget_s=20.0):
                       f"host has {os.cpu_count()} logical CPUs"}
 
 
-def secondary_verify(pk, torch, dev, batch=64, hkv=8, iters=20):
+def secondary_verify(pk, torch, dev, batch=64, hkv=8, iters=20, warmup=3):
     """Speculative verify: KV GB/s of run() on the verify workload."""
     w = W.config4(batch=batch, num_kv_heads=hkv)
     tensors = _device_inputs(w, dev)
     p = pk.verify_plan(w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 4, w.num_qo_heads,
                        w.num_kv_heads, w.head_dim, w.page_size, dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
+    for _ in range(warmup):
         p.run(*tensors)
     ms = time_kernel(pk, p, tensors, iters)
     nbytes = kv_bytes(w)
@@ -157,7 +180,7 @@ def main():
     args = ap.parse_args()
     if args.profile:
         args.steps, args.warmup, args.kernel_iters = 3, 1, 3
-        args.no_cpu_baseline, args.secondary = True, False
+        args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-KV prefill path has no multi-GPU "
               "component here (run with --gpus 1)", file=sys.stderr)
@@ -210,11 +233,13 @@ def main():
                    "head_dim": w.head_dim, "causal": w.causal, "window_left": w.window_left,
                    "total_q": w.total_q, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(),
                      "kernel": "attn_kernel (prefill tile)", "kernel_ms": kernel_ms},
     }
     if args.secondary:
-        result["secondary"] = {"verify": secondary_verify(pk, torch, dev)}
+        n = 3 if args.profile else 20
+        result["secondary"] = {"verify": secondary_verify(pk, torch, dev, iters=n, warmup=1 if args.profile else 3)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result))

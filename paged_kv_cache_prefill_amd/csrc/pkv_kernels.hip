@@ -324,6 +324,15 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 
     // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
     const int jl = j0 + wn * NW + 4 * g;
+    // Lazy rescaling: exponents are taken against a reference m_run per row
+    // that moves only when a score exceeds it by more than kTau (log2 units),
+    // so every p stays <= 2^kTau; the reference cancels in o = sum p v / sum p
+    // and is added back into lse.  The common case needs no cross-lane work:
+    // each lane tests its own scores against the (row-uniform) reference, and
+    // only when some lane of the wave fails does the wave reduce the row
+    // maxima over the four lane groups of a row and rescale.
+    float mloc[QB];
+    bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = kNegInf;
@@ -340,21 +349,24 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           mx = fmaxf(mx, x);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescaling: exponents are taken against a reference m_run that
-      // only moves when some row of the wave sees a score more than kTau
-      // (log2 units) above it, so every p stays <= 2^kTau.  The reference
-      // cancels in o = sum p v / sum p and is added back into lse.
-      const float mxs = mx * a.scale_log2;
-      if (wave_any(mxs > m_run[qb] + kTau)) {
-        const float m_new = fmaxf(m_run[qb], mxs);
+      mloc[qb] = mx * a.scale_log2;
+      grow = grow || (mloc[qb] > m_run[qb] + kTau);
+    }
+    if (wave_any(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = fmaxf(mloc[qb], __shfl_xor(mloc[qb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qb], mx);
         const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run[qb] - m_new);
         m_run[qb] = m_new;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
       float rs = 0.f;
 #pragma unroll
