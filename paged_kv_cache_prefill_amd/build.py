@@ -24,6 +24,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (the short-query tiles are LDS-limited to
+    # one work group per CU, where the compiler would otherwise shuttle
+    # accumulators between AGPRs and VGPRs inside the key loop)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
               "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]

@@ -260,7 +260,8 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     kin[m] = lslot * a.k_s_tok + koff[m];
     vin[m] = lslot * a.v_s_tok + voff[m];
   }
-  KeyLoc loc[NI];           // page (and slot, general path) of each lane row of the next tile
+  // page (and, on the general path, slot) of each lane row of the next tile
+  uint32_t lpage[NI], lslot[NI];
   uint32_t tile_page = 0;   // PM 2: the next tile's single page
   const int32_t* ptab = a.pages + rq.page_off;
   auto fetch_pages = [&](int j0) {
@@ -268,14 +269,20 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     if (PM == 1 && fast) {
       const int32_t* pt = ptab + (j0 >> a.page_shift);
 #pragma unroll
-      for (int m = 0; m < NI; ++m) loc[m].page = (uint32_t)pt[lrow[m] >> a.page_shift];
+      for (int m = 0; m < NI; ++m) {
+        lpage[m] = (uint32_t)pt[lrow[m] >> a.page_shift];
+        lslot[m] = (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
+      }
     } else if (PM == 2 && fast) {
       tile_page = (uint32_t)ptab[j0 >> a.page_shift];
     } else {
 #pragma unroll
-      for (int m = 0; m < NI; ++m)
-        loc[m] = locate_key(ptab, (uint32_t)min(j0 + lrow[m], last_key), a.page_magic,
-                            a.page_shift, (uint32_t)a.page_size);
+      for (int m = 0; m < NI; ++m) {
+        const KeyLoc l = locate_key(ptab, (uint32_t)min(j0 + lrow[m], last_key), a.page_magic,
+                                    a.page_shift, (uint32_t)a.page_size);
+        lpage[m] = l.page;
+        lslot[m] = l.slot;
+      }
     }
   };
   auto issue_tile = [&](int j0, uint4* kdst, uint4* vdst) {
@@ -285,8 +292,8 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const uint64_t vt0 = (uint64_t)tile_page * a.v_s_page + slot0 * a.v_s_tok;
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const uint64_t ko = PM == 1 ? (uint64_t)loc[m].page * a.k_s_page + kin[m] : kt0 + kin[m];
-        const uint64_t vo = PM == 1 ? (uint64_t)loc[m].page * a.v_s_page + vin[m] : vt0 + vin[m];
+        const uint64_t ko = PM == 1 ? (uint64_t)lpage[m] * a.k_s_page + kin[m] : kt0 + kin[m];
+        const uint64_t vo = PM == 1 ? (uint64_t)lpage[m] * a.v_s_page + vin[m] : vt0 + vin[m];
         const int base = (m * NWAVE + wave) * 64;
         load_lds16(kp + ko, kdst + base);
         load_lds16(vp + vo, vdst + base);
@@ -294,8 +301,9 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const uint64_t ko = key_offset(loc[m], a.k_s_page, a.k_s_tok, koff[m]);
-        const uint64_t vo = key_offset(loc[m], a.v_s_page, a.v_s_tok, voff[m]);
+        const KeyLoc l{lpage[m], lslot[m]};
+        const uint64_t ko = key_offset(l, a.k_s_page, a.k_s_tok, koff[m]);
+        const uint64_t vo = key_offset(l, a.v_s_page, a.v_s_tok, voff[m]);
         const int base = (m * NWAVE + wave) * 64;
         load_lds16(kp + ko, kdst + base);
         load_lds16(vp + vo, vdst + base);
