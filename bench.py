@@ -1,6 +1,6 @@
 """Benchmark: paged-KV attention prefill on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--secondary]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-coverage]
 
 One step = plan (host validation + scheduling + one async copy) and run
 (attention + split merge) over the paged batch-prefill workload: batch 8,
@@ -11,6 +11,9 @@ step (4 * head_dim flops per visible (query, key) pair per q head).
 
 Prints ONE JSON line.  `roofline` covers the attention kernel: its average
 duration comes from HIP events around each launch on the stream it runs on.
+`coverage` times every other workload of the path (windowed prefill,
+non-causal windows at page 1024 and 16, speculative verify at every batch and
+kv-head count, long-context split-KV with merge) against its roofline.
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
 workload (rank 0, N = 1 only).
 """
@@ -148,19 +151,81 @@ def cpu_baseline(w, budget_s=20.0):
                       f"host has {os.cpu_count()} logical CPUs"}
 
 
-def secondary_verify(pk, torch, dev, batch=64, hkv=8, iters=20, warmup=3):
-    """Speculative verify: KV GB/s of run() on the verify workload."""
-    w = W.config4(batch=batch, num_kv_heads=hkv)
-    tensors = _device_inputs(w, dev)
-    p = pk.verify_plan(w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 4, w.num_qo_heads,
-                       w.num_kv_heads, w.head_dim, w.page_size, dtype=torch.bfloat16, device=dev)
-    for _ in range(warmup):
-        p.run(*tensors)
-    ms = time_kernel(pk, p, tensors, iters)
-    nbytes = kv_bytes(w)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": w.name, "ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
-            "bytes": nbytes, "work_items": p.info["num_work_items"]}
+def _random_pools(w, dev, copies, seed):
+    """Timing-only pools of the workload's shape: N(0, 1) drawn on the device."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+    shape = (w.num_pages, w.page_size, w.num_kv_heads, w.head_dim)
+    mk = lambda: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+    q = torch.randn((w.total_q, w.num_qo_heads, w.head_dim), generator=g, device=dev,
+                    dtype=torch.float32).to(dt)
+    return q, [(mk(), mk()) for _ in range(copies)]
+
+
+def time_rotating(p, q, pools, iters, warmup=2):
+    """Average run() time (ms) from HIP events, cycling through K/V pool copies."""
+    import torch
+    s = torch.cuda.current_stream()
+    o = torch.empty((p.total_q_rows, p.num_qo_heads, p.head_dim), dtype=p.dtype, device=q.device)
+    lse = torch.empty((p.total_q_rows, p.num_qo_heads), dtype=torch.float32, device=q.device)
+    for i in range(warmup):
+        k, v = pools[i % len(pools)]
+        p.run(q, k, v, out=o, lse=lse)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        k, v = pools[i % len(pools)]
+        a.record(s)
+        p.run(q, k, v, out=o, lse=lse)
+        b.record(s)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def coverage(pk, torch, dev, iters=20):
+    """Every workload of the path, each against the roofline that binds it:
+    workloads above the ridge point (peak flops / peak bytes, about 312 flop per
+    byte) report algorithmic TFLOP/s against the bf16 MFMA peak, the others
+    (verify, decode over long contexts, narrow windows) algorithmic GB/s (K/V
+    rows any query row can see, plus q, o, lse) against the HBM peak.  K/V pools rotate so that at least 512 MB is touched
+    between reuses of a pool (the 256 MB Infinity Cache cannot hold them)."""
+    rows = []
+    cases = [("single_contiguous_w-1", W.config1(values=False), {}),
+             ("single_contiguous_w31", W.config1(window_left=31, values=False), {}),
+             ("paged_prefill_b8_w127", W.config2(window_left=127, values=False), {})]
+    for page in (1024, 16):
+        for wl in (0, 31, 127, 8192):
+            cases.append((f"noncausal_window_b4_p{page}_w{wl}",
+                          W.config3(window_left=wl, page_size=page, values=False), {}))
+    for b in (4, 16, 64):
+        for h in (4, 8):
+            cases.append((f"verify_b{b}_hkv{h}", W.config4(batch=b, num_kv_heads=h, values=False), {}))
+    for ql in (1, 64):
+        for wl in (-1, 4095):
+            cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",
+                          W.config5(qo_len=ql, window_left=wl, values=False),
+                          {"num_kv_chunks": W.CONFIG5_CHUNKS}))
+    for i, (name, w, opts) in enumerate(cases):
+        dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+        nbytes = kv_bytes(w)
+        copies = max(1, min(16, -(-512_000_000 // max(nbytes, 1))))
+        q, pools = _random_pools(w, dev, copies, seed=7000 + i)
+        p = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
+        ms = time_rotating(p, q, pools, iters)
+        flops = attention_flops(w)
+        # the roofline that binds: arithmetic intensity against the ridge point
+        hbm_bound = flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        rec = {"workload": name, "ms": ms, "TFLOP/s": flops / ms / 1e9,
+               "GB/s": nbytes / ms / 1e6, "bound": "hbm" if hbm_bound else "mfma",
+               "pool_copies": copies, "work_items": p.info["num_work_items"],
+               "split_tiles": p.info["num_merge_items"]}
+        rec["frac"] = rec["GB/s"] / PEAK_HBM_GBS if hbm_bound else rec["TFLOP/s"] / PEAK_BF16_TFLOPS
+        rows.append(rec)
+        del q, pools, p
+        torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -170,7 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--window-left", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--secondary", action="store_true", help="also time speculative verify")
+    ap.add_argument("--no-coverage", action="store_true",
+                    help="skip timing the other workloads against their rooflines")
     ap.add_argument("--kernel-iters", type=int, default=50)
     ap.add_argument("--profile", action="store_true",
                     help="short run for profilers: 3 steps, 1 warmup, no baselines")
@@ -180,7 +246,7 @@ def main():
     args = ap.parse_args()
     if args.profile:
         args.steps, args.warmup, args.kernel_iters = 3, 1, 3
-        args.no_cpu_baseline = True
+        args.no_cpu_baseline = args.no_coverage = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-KV prefill path has no multi-GPU "
               "component here (run with --gpus 1)", file=sys.stderr)
@@ -237,9 +303,8 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel": "attn_kernel (prefill tile)", "kernel_ms": kernel_ms},
     }
-    if args.secondary:
-        n = 3 if args.profile else 20
-        result["secondary"] = {"verify": secondary_verify(pk, torch, dev, iters=n, warmup=1 if args.profile else 3)}
+    if not args.no_coverage:
+        result["coverage"] = coverage(pk, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result))

@@ -306,18 +306,31 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     }
   }
 
-  // ---- split decision
+  // ---- split decision: fixed chunk boundaries when asked for, and when the
+  // launch would have fewer than kTargetTasks work groups, chunks longer than
+  // the average share are split further (partials are merged either way)
   auto cost = [&](const RowTask& t) -> int64_t {
     return t.key_lo > t.key_hi ? 0 : (t.key_hi + 1 - t.tile_begin + NK - 1) / NK;
   };
   int64_t chunk_tiles = 0;  // 0: no automatic split
-  if (o.num_kv_chunks == 0 && (int64_t)tasks.size() < kTargetTasks) {
-    int64_t total = 0;
-    for (const RowTask& t : tasks) total += cost(t);
-    const int64_t min_tiles = (kind == TILE_PREFILL) ? 8 : 4;
-    chunk_tiles = std::max<int64_t>(min_tiles, (total + kTargetTasks - 1) / kTargetTasks);
+  {
+    int64_t n = 0, total = 0;
+    for (const RowTask& t : tasks) {
+      total += cost(t);
+      if (o.num_kv_chunks > 0 && t.key_lo <= t.key_hi) {   // requested chunks the range meets
+        const int64_t L = S->reqs[t.b].kv_len;
+        int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
+        clen = std::max<int64_t>(NK, (clen + NK - 1) / NK * NK);
+        n += t.key_hi / clen - t.key_lo / clen + 1;
+      } else {
+        n += 1;
+      }
+    }
+    if (n < kTargetTasks) {
+      const int64_t min_tiles = (kind == TILE_PREFILL) ? 8 : 4;
+      chunk_tiles = std::max<int64_t>(min_tiles, (total + kTargetTasks - 1) / kTargetTasks);
+    }
   }
-
   std::vector<WorkItem> items;
   std::vector<int32_t> costs;
   items.reserve(tasks.size() * 2);
@@ -344,24 +357,30 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
       continue;
     }
     chunks.clear();
+    // base chunks: the requested equal split in the request's key coordinates
+    // (tile-aligned), else the whole visible range
+    auto add = [&](int64_t a, int64_t e) {   // sub-split [a, e) at tile-aligned steps
+      if (a >= e) return;
+      if (chunk_tiles <= 0) {
+        chunks.emplace_back((int32_t)a, (int32_t)e);
+        return;
+      }
+      const int64_t step = chunk_tiles * NK;
+      int64_t c = a;
+      while (c < e) {
+        const int64_t nxt = std::min<int64_t>((c / NK * NK) + step, e);
+        chunks.emplace_back((int32_t)c, (int32_t)nxt);
+        c = nxt;
+      }
+    };
     if (o.num_kv_chunks > 0) {
       const int64_t L = S->reqs[t.b].kv_len;
       int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
       clen = std::max<int64_t>(NK, (clen + NK - 1) / NK * NK);
-      for (int64_t c0 = 0; c0 < L; c0 += clen) {
-        const int64_t a = std::max<int64_t>(c0, t.key_lo);
-        const int64_t e = std::min<int64_t>(c0 + clen, (int64_t)t.key_hi + 1);
-        if (a < e) chunks.emplace_back((int32_t)a, (int32_t)e);
-      }
-    } else if (chunk_tiles > 0 && cost(t) > chunk_tiles) {
-      const int64_t step = chunk_tiles * NK;
-      for (int64_t c0 = t.tile_begin; c0 <= t.key_hi; c0 += step) {
-        const int64_t a = std::max<int64_t>(c0, t.key_lo);
-        const int64_t e = std::min<int64_t>(c0 + step, (int64_t)t.key_hi + 1);
-        if (a < e) chunks.emplace_back((int32_t)a, (int32_t)e);
-      }
+      for (int64_t c0 = 0; c0 < L; c0 += clen)
+        add(std::max<int64_t>(c0, t.key_lo), std::min<int64_t>(c0 + clen, (int64_t)t.key_hi + 1));
     } else {
-      chunks.emplace_back(t.key_lo, t.key_hi + 1);
+      add(t.key_lo, (int64_t)t.key_hi + 1);
     }
     if (chunks.size() == 1) {
       emit(t, chunks[0].first, chunks[0].second, t.tile_begin, -1);
