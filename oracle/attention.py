@@ -14,6 +14,7 @@ matmul / exp / log as the only library steps:
 * ``attention``         -- masked softmax(sm_scale * Q K^T) V with GQA, plus LSE.
 * ``attention_bruteforce`` -- the same definition as per-element Python loops.
 * ``merge_states`` / ``merge_many`` -- combining partial (o, lse) states.
+* ``append_paged_kv``   -- writing new K/V rows into their pages.
 
 Sources (web pages of the AMD-Ecosystem FlashInfer fork):
   [W]  PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
@@ -285,3 +286,23 @@ def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
             lse[ri, hi_] = m + np.log(total)
             o[ri, hi_] = (e / total) @ vb[ok]
     return o, lse
+
+
+def append_paged_kv(k_pool, v_pool, append_k, append_v, batch_indices, positions,
+                    kv_indptr, kv_page_indices, page_size):
+    """Write new key/value rows into a paged cache, returning updated copies.
+
+    Token t belongs to request batch_indices[t] at logical position
+    positions[t]; it lands on page kv_page_indices[kv_indptr[b] + pos // P],
+    slot pos % P (the same page table attention reads, PR #399's note that
+    appends write scattered pages).  Rows are copied exactly; every other slot
+    is left untouched.  append_k / append_v: [tokens, Hkv, D].
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    for t in range(len(batch_indices)):
+        b, pos = int(batch_indices[t]), int(positions[t])
+        page = int(kv_page_indices[int(kv_indptr[b]) + pos // page_size])
+        k_out[page, pos % page_size] = append_k[t]
+        v_out[page, pos % page_size] = append_v[t]
+    return k_out, v_out

@@ -470,3 +470,46 @@ def test_sampled_rows_match_full_oracle():
     o, lse = oracle.attention_rows(**prob, causal=True, window_left=-1, sm_scale=0.6, b=1,
                                    rows=[0, 8], heads=[1], kv_begin=4, kv_end=9)
     np.testing.assert_allclose(o[:, 0], part[0][[6, 14], 1], atol=1e-12)
+
+
+def test_append_hand_example():
+    """Two requests, page size 2: hand-placed destinations of three new tokens."""
+    pool = np.zeros((4, 2, 1, 1))
+    indptr = np.array([0, 2, 3])
+    pages = np.array([3, 0, 2])        # request 0: pages 3, 0; request 1: page 2
+    ak = np.array([[[1.0]], [[2.0]], [[3.0]]])
+    av = -ak
+    # token 0 -> request 0 pos 2 -> page 0 slot 0; token 1 -> request 0 pos 1 -> page 3 slot 1;
+    # token 2 -> request 1 pos 1 -> page 2 slot 1
+    k, v = oracle.append_paged_kv(pool, pool, ak, av, [0, 0, 1], [2, 1, 1], indptr, pages, 2)
+    want = np.zeros((4, 2))
+    want[0, 0], want[3, 1], want[2, 1] = 1.0, 2.0, 3.0
+    np.testing.assert_array_equal(k[:, :, 0, 0], want)
+    np.testing.assert_array_equal(v[:, :, 0, 0], -want)
+    assert np.all(pool == 0)           # input untouched
+
+
+def test_append_then_gather_round_trip():
+    rng = np.random.default_rng(30)
+    prob = small_problem(rng, [3, 5], [20, 33], 4, 2, 8, 16)
+    L = oracle.kv_lengths(prob["kv_indptr"], prob["kv_last_page_len"], 16)
+    # append the last 4 and 7 keys of the two requests
+    bi = np.array([0] * 4 + [1] * 7)
+    pos = np.concatenate([np.arange(L[0] - 4, L[0]), np.arange(L[1] - 7, L[1])])
+    ak = rng.standard_normal((11, 2, 8))
+    av = rng.standard_normal((11, 2, 8))
+    k, v = oracle.append_paged_kv(prob["k_pool"], prob["v_pool"], ak, av, bi, pos,
+                                  prob["kv_indptr"], prob["kv_page_indices"], 16)
+    for b, (lo, n) in enumerate([(0, 4), (4, 7)]):
+        kb = oracle.gather_request_kv(k, prob["kv_indptr"], prob["kv_page_indices"], b, L[b], 16)
+        old = oracle.gather_request_kv(prob["k_pool"], prob["kv_indptr"], prob["kv_page_indices"],
+                                       b, L[b], 16)
+        np.testing.assert_array_equal(kb[L[b] - n:], ak[lo:lo + n])
+        np.testing.assert_array_equal(kb[:L[b] - n], old[:L[b] - n])
+    # slots no token targets are unchanged
+    touched = np.zeros(prob["k_pool"].shape[:2], dtype=bool)
+    for t in range(11):
+        b = bi[t]
+        page = prob["kv_page_indices"][prob["kv_indptr"][b] + pos[t] // 16]
+        touched[page, pos[t] % 16] = True
+    np.testing.assert_array_equal(k[~touched], prob["k_pool"][~touched])
