@@ -225,7 +225,54 @@ def coverage(pk, torch, dev, iters=20):
         rows.append(rec)
         del q, pools, p
         torch.cuda.empty_cache()
+    for name, w, per_req in (("append_prefill_b8", W.config2(values=False), None),
+                             ("append_verify_b64_hkv8", W.config4(batch=64, values=False), 4)):
+        rows.append(time_append(pk, torch, dev, name, w, per_req, iters))
     return rows
+
+
+def time_append(pk, torch, dev, name, w, per_req, iters):
+    """append_kv of the workload's last `per_req` keys per request (all keys when
+    None) into its paged pools.  Algorithmic bytes: the new K and V rows read
+    once and written once, plus 8 bytes of (request, position) per token."""
+    dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+    bi, pos = [], []
+    for b in range(w.batch_size):
+        L = int(w.kv_lens[b])
+        n = L if per_req is None else min(per_req, L)
+        bi.append(np.full(n, b, np.int32))
+        pos.append(np.arange(L - n, L, dtype=np.int32))
+    bi = torch.from_numpy(np.concatenate(bi)).to(dev)
+    pos = torch.from_numpy(np.concatenate(pos)).to(dev)
+    tokens = bi.numel()
+    indptr = torch.from_numpy(w.kv_indptr.astype(np.int32)).to(dev)
+    pages = torch.from_numpy(w.kv_page_indices.astype(np.int32)).to(dev)
+    shape = (w.num_pages, w.page_size, w.num_kv_heads, w.head_dim)
+    k = torch.zeros(shape, dtype=dt, device=dev)
+    v = torch.zeros(shape, dtype=dt, device=dev)
+    row_bytes = w.num_kv_heads * w.head_dim * 2
+    nbytes = tokens * (4 * row_bytes + 8)
+    copies = max(1, min(8, -(-512_000_000 // max(2 * tokens * row_bytes, 1))))
+    srcs = [(torch.randn((tokens, w.num_kv_heads, w.head_dim), device=dev).to(dt),
+             torch.randn((tokens, w.num_kv_heads, w.head_dim), device=dev).to(dt))
+            for _ in range(copies)]
+    s = torch.cuda.current_stream()
+    for i in range(2):
+        pk.append_kv(*srcs[i % copies], bi, pos, indptr, pages, k, v)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record(s)
+        pk.append_kv(*srcs[i % copies], bi, pos, indptr, pages, k, v)
+        b.record(s)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    rec = {"workload": name, "ms": ms, "GB/s": nbytes / ms / 1e6, "bound": "hbm",
+           "tokens": tokens, "source_copies": copies}
+    rec["frac"] = rec["GB/s"] / PEAK_HBM_GBS
+    del srcs, k, v
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():

@@ -179,6 +179,36 @@ pkv_status pkv_merge_states(const void* o_a, const float* lse_a, const void* o_b
                             pkv_dtype dtype, void* stream);
 
 /*
+ * append_kv: write new key/value rows into a paged cache, the step before an
+ * attention call over the same page table (PR #399, Architecture notes: an
+ * append writes scattered pages).  Token t belongs to request
+ * batch_indices[t] at logical position positions[t] and lands on page
+ * kv_page_indices[kv_indptr[b] + positions[t] / page_size], slot
+ * positions[t] % page_size; K and V rows are copied bit for bit.
+ *   append_k, append_v: [num_tokens, num_kv_heads, head_dim] device arrays
+ *     (token / head strides in elements, head_dim packed).
+ *   batch_indices, positions [num_tokens], kv_indptr [batch_size + 1],
+ *     kv_page_indices [num_indices]: device int32 arrays.
+ *   k, v: page pools as in pkv_run, written in place.
+ *   err_count: optional device int32, incremented once for every token whose
+ *     request, position, page-table entry or page id is out of range; such a
+ *     token is skipped and nothing outside the arrays is read or written.
+ * Refused on the host: dtype not fp16/bf16, head_dim not a positive multiple
+ * of 8, k and v shapes that differ, strides or alignment as for pkv_run.
+ */
+pkv_status pkv_append_kv(const void* append_k, int64_t ak_s_tok, int64_t ak_s_head,
+                         const void* append_v, int64_t av_s_tok, int64_t av_s_head,
+                         int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         const int32_t* batch_indices, const int32_t* positions,
+                         const int32_t* kv_indptr, int32_t batch_size,
+                         const int32_t* kv_page_indices, int64_t num_indices,
+                         void* k, int64_t k_pages, int32_t k_page_size, int64_t k_s_page,
+                         int64_t k_s_tok, int64_t k_s_head,
+                         void* v, int64_t v_pages, int32_t v_page_size, int64_t v_s_page,
+                         int64_t v_s_tok, int64_t v_s_head,
+                         pkv_dtype dtype, int32_t* err_count, void* stream);
+
+/*
  * debug_gather: write the logical K and V rows of every planned request,
  * [sum kv_len, kv_heads, head_dim] in request order, through the same page
  * address path the attention kernel reads (for bit-exact gather checks).

@@ -25,7 +25,8 @@ import os
 
 import numpy as np
 
-__all__ = ["plan", "plan_host", "verify_plan", "workspace_size", "merge_states", "Plan",
+__all__ = ["plan", "plan_host", "verify_plan", "workspace_size", "merge_states", "append_kv",
+           "Plan",
            "PkvError", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,12 +96,18 @@ def load_library():
     lib.pkv_debug_gather.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, i64,
                                      vp, i64, i32, i32, i32, i64, i64, i64,
                                      ctypes.c_int, vp, vp, i64, vp]
+    lib.pkv_append_kv.argtypes = [vp, i64, i64, vp, i64, i64, i64, i32, i32,
+                                  vp, vp, vp, i32, vp, i64,
+                                  vp, i64, i32, i64, i64, i64,
+                                  vp, i64, i32, i64, i64, i64,
+                                  ctypes.c_int, vp, vp]
     lib.pkv_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.pkv_plan_get_work.argtypes = [vp, pi32, i64, ctypes.POINTER(i64)]
     lib.pkv_plan_destroy.argtypes = [vp]
     lib.pkv_plan_destroy.restype = None
     for name in ("pkv_workspace_size", "pkv_plan", "pkv_run", "pkv_merge_states",
-                 "pkv_debug_gather", "pkv_plan_get_info", "pkv_plan_get_work"):
+                 "pkv_debug_gather", "pkv_append_kv", "pkv_plan_get_info",
+                 "pkv_plan_get_work"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -422,3 +429,55 @@ def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
                                 heads, dim, _dtype_code(o_a.dtype),
                                 ctypes.c_void_p(stream.cuda_stream)))
     return out, lse_out
+
+
+def append_kv(append_k, append_v, batch_indices, positions, kv_indptr, kv_page_indices,
+              paged_k, paged_v, kv_layout="NHD", err_count=None, stream=None):
+    """Write new K/V rows into their pages (in place) and return (paged_k, paged_v).
+
+    append_k / append_v: [tokens, num_kv_heads, head_dim] in the cache's dtype, head_dim
+    packed.  batch_indices, positions [tokens], kv_indptr [batch + 1], kv_page_indices:
+    int32 tensors on the cache's device.  Token t goes to page
+    kv_page_indices[kv_indptr[b] + pos // page_size], slot pos % page_size.  err_count
+    (optional int32 device tensor of one element) counts tokens skipped as out of range."""
+    torch = _torch()
+    lib = load_library()
+    k = Plan._cache_view(paged_k, kv_layout)
+    v = Plan._cache_view(paged_v, kv_layout)
+    dev = paged_k.device
+    if paged_v.device != dev or paged_k.dtype != paged_v.dtype:
+        raise PkvError(PKV_EMISMATCH, "paged_k / paged_v: expected one device and dtype")
+    for name, t in (("append_k", append_k), ("append_v", append_v)):
+        if t.dim() != 3 or t.dtype != paged_k.dtype or t.device != dev:
+            raise PkvError(PKV_EMISMATCH, f"{name}: expected a [tokens, heads, head_dim] "
+                                          f"{paged_k.dtype} tensor on {dev}")
+        if t.stride(2) != 1:
+            raise PkvError(PKV_ELAYOUT, f"{name}: head_dim stride must be 1")
+        if tuple(t.shape) != (append_k.shape[0], k.shape[2], k.shape[3]):
+            raise PkvError(PKV_EMISMATCH, f"{name}: expected [{append_k.shape[0]}, "
+                                          f"{k.shape[2]}, {k.shape[3]}], given {tuple(t.shape)}")
+    tokens = append_k.shape[0]
+    for name, t, n in (("batch_indices", batch_indices, tokens), ("positions", positions, tokens),
+                       ("kv_indptr", kv_indptr, None), ("kv_page_indices", kv_page_indices, None)):
+        if t.dtype != torch.int32 or t.device != dev or t.dim() != 1 or not t.is_contiguous():
+            raise PkvError(PKV_EINVAL, f"{name}: expected a packed 1-D int32 tensor on {dev}")
+        if n is not None and t.shape[0] != n:
+            raise PkvError(PKV_EMISMATCH, f"{name}: expected {n} entries, given {t.shape[0]}")
+    if kv_indptr.shape[0] < 1:
+        raise PkvError(PKV_EINVAL, "kv_indptr: expected batch + 1 >= 1 entries")
+    if err_count is not None and (err_count.dtype != torch.int32 or err_count.device != dev
+                                  or err_count.numel() < 1):
+        raise PkvError(PKV_EINVAL, "err_count: expected an int32 device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(lib.pkv_append_kv(
+        append_k.data_ptr(), append_k.stride(0), append_k.stride(1),
+        append_v.data_ptr(), append_v.stride(0), append_v.stride(1),
+        tokens, k.shape[2], k.shape[3],
+        batch_indices.data_ptr(), positions.data_ptr(), kv_indptr.data_ptr(),
+        kv_indptr.shape[0] - 1, kv_page_indices.data_ptr(), kv_page_indices.shape[0],
+        k.data_ptr(), k.shape[0], k.shape[1], k.stride(0), k.stride(1), k.stride(2),
+        v.data_ptr(), v.shape[0], v.shape[1], v.stride(0), v.stride(1), v.stride(2),
+        _dtype_code(paged_k.dtype), err_count.data_ptr() if err_count is not None else None,
+        ctypes.c_void_p(stream.cuda_stream)))
+    return paged_k, paged_v

@@ -769,6 +769,83 @@ pkv_status pkv_merge_states(const void* o_a, const float* lse_a, const void* o_b
   return PKV_OK;
 }
 
+pkv_status pkv_append_kv(const void* append_k, int64_t ak_s_tok, int64_t ak_s_head,
+                         const void* append_v, int64_t av_s_tok, int64_t av_s_head,
+                         int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         const int32_t* batch_indices, const int32_t* positions,
+                         const int32_t* kv_indptr, int32_t batch_size,
+                         const int32_t* kv_page_indices, int64_t num_indices,
+                         void* k, int64_t k_pages, int32_t k_page_size, int64_t k_s_page,
+                         int64_t k_s_tok, int64_t k_s_head,
+                         void* v, int64_t v_pages, int32_t v_page_size, int64_t v_s_page,
+                         int64_t v_s_tok, int64_t v_s_head,
+                         pkv_dtype dtype, int32_t* err_count, void* stream) {
+  g_err.clear();
+  if (dtype != PKV_FP16 && dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "dtype: expected fp16 or bf16, given %s", dtype_name(dtype));
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens: expected >= 0, given %lld", (long long)num_tokens);
+  if (num_kv_heads <= 0) return fail(PKV_EINVAL, "num_kv_heads: expected > 0, given %d", num_kv_heads);
+  if (head_dim <= 0 || head_dim % 8)
+    return fail(PKV_EINVAL, "head_dim: expected a positive multiple of 8, given %d", head_dim);
+  if (batch_size < 0) return fail(PKV_EINVAL, "batch_size: expected >= 0, given %d", batch_size);
+  if (num_indices < 0) return fail(PKV_EINVAL, "num_indices: expected >= 0, given %lld", (long long)num_indices);
+  if (k_page_size < 1) return fail(PKV_EINVAL, "page_size: expected >= 1, given %d", k_page_size);
+  if (v_page_size != k_page_size)
+    return fail(PKV_EMISMATCH, "v page_size: k has %d, given %d", k_page_size, v_page_size);
+  if (v_pages != k_pages)
+    return fail(PKV_EMISMATCH, "v num_pages: k has %lld, given %lld", (long long)k_pages, (long long)v_pages);
+  if (num_tokens == 0) return PKV_OK;
+  if (!append_k || !append_v || !batch_indices || !positions || !kv_indptr ||
+      (num_indices > 0 && !kv_page_indices) || !k || !v)
+    return fail(PKV_EINVAL, "append_kv: expected device pointers, given NULL");
+  for (const void* ptr : {append_k, append_v, (const void*)k, (const void*)v})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return fail(PKV_ELAYOUT, "append_kv: expected 16-byte aligned k / v / append pointers");
+  for (int64_t st : {ak_s_tok, ak_s_head, av_s_tok, av_s_head})
+    if (st < 0 || st % 8)
+      return fail(PKV_ELAYOUT, "append strides: expected non-negative multiples of 8 elements, given %lld",
+                  (long long)st);
+  const int64_t in_k = (int64_t)(k_page_size - 1) * k_s_tok + (int64_t)(num_kv_heads - 1) * k_s_head + head_dim;
+  const int64_t in_v = (int64_t)(v_page_size - 1) * v_s_tok + (int64_t)(num_kv_heads - 1) * v_s_head + head_dim;
+  for (int64_t st : {k_s_page, k_s_tok, k_s_head, v_s_page, v_s_tok, v_s_head})
+    if (st < 0 || st % 8 || st >= (1ll << 31))
+      return fail(PKV_ELAYOUT, "cache strides: expected non-negative multiples of 8 elements below 2^31, "
+                               "given %lld", (long long)st);
+  if (in_k >= (1ll << 31) || in_v >= (1ll << 31))
+    return fail(PKV_ELAYOUT, "cache strides: one page must span fewer than 2^31 elements");
+  AppendArgs a;
+  a.ak = append_k;
+  a.av = append_v;
+  a.k = k;
+  a.v = v;
+  a.batch_indices = batch_indices;
+  a.positions = positions;
+  a.kv_indptr = kv_indptr;
+  a.pages = kv_page_indices;
+  a.err_count = err_count;
+  a.num_tokens = num_tokens;
+  a.num_indices = num_indices;
+  a.num_pages = k_pages;
+  a.ak_s_tok = ak_s_tok;
+  a.ak_s_head = ak_s_head;
+  a.av_s_tok = av_s_tok;
+  a.av_s_head = av_s_head;
+  a.k_s_page = (uint32_t)k_s_page;
+  a.k_s_tok = (uint32_t)k_s_tok;
+  a.k_s_head = (uint32_t)k_s_head;
+  a.v_s_page = (uint32_t)v_s_page;
+  a.v_s_tok = (uint32_t)v_s_tok;
+  a.v_s_head = (uint32_t)v_s_head;
+  a.heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.batch = batch_size;
+  a.page_size = k_page_size;
+  page_divider((uint32_t)k_page_size, &a.page_magic, &a.page_shift);
+  hipError_t e = launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "append launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_t k_page_size,
                             int32_t k_heads, int32_t k_dim, int64_t k_s_page, int64_t k_s_tok,
                             int64_t k_s_head, const void* v, int64_t v_pages,

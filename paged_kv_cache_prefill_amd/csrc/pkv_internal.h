@@ -118,6 +118,24 @@ struct GatherArgs {
   int32_t batch;
 };
 
+struct AppendArgs {
+  const void* ak;
+  const void* av;
+  void* k;
+  void* v;
+  const int32_t* batch_indices;
+  const int32_t* positions;
+  const int32_t* kv_indptr;
+  const int32_t* pages;
+  int32_t* err_count;      // nullable
+  int64_t num_tokens, num_indices, num_pages;
+  int64_t ak_s_tok, ak_s_head, av_s_tok, av_s_head;
+  uint32_t k_s_page, k_s_tok, k_s_head;
+  uint32_t v_s_page, v_s_tok, v_s_head;
+  int32_t heads, head_dim, batch, page_size;
+  uint32_t page_magic, page_shift;
+};
+
 // dtype: 0 fp16, 1 bf16, 2 fp32 (merge_states only).
 hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
                             hipStream_t stream);
@@ -129,5 +147,6 @@ hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,
                                int32_t head_dim, hipStream_t stream);
 hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a,
                                hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
 }  // namespace pkv

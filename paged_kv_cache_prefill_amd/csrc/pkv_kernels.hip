@@ -688,6 +688,55 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// append: new K/V rows into their pages
+// ---------------------------------------------------------------------------
+// One thread per (token, head, 16-byte chunk); every index is range-checked
+// before it is used, so a bad token is counted and skipped.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int chunks = a.head_dim / 8;
+  const int64_t per_tok = (int64_t)a.heads * chunks;
+  const int64_t total = a.num_tokens * per_tok;
+  const char* ak = static_cast<const char*>(a.ak);
+  const char* av = static_cast<const char*>(a.av);
+  char* kp = static_cast<char*>(a.k);
+  char* vp = static_cast<char*>(a.v);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = idx / per_tok;
+    const int rem = (int)(idx - t * per_tok);
+    const int h = rem / chunks;
+    const int c = rem - h * chunks;
+    const int32_t b = a.batch_indices[t];
+    const int32_t pos = a.positions[t];
+    bool ok = b >= 0 && b < a.batch && pos >= 0;
+    uint32_t page = 0, slot = 0;
+    if (ok) {
+      const int32_t first = a.kv_indptr[b];
+      const int32_t n = a.kv_indptr[b + 1] - first;
+      const uint32_t pidx = (uint32_t)(((uint64_t)(uint32_t)pos * a.page_magic) >> a.page_shift);
+      ok = first >= 0 && (int64_t)pidx < (int64_t)n && (int64_t)first + pidx < a.num_indices;
+      if (ok) {
+        const int32_t pg = a.pages[first + pidx];
+        ok = pg >= 0 && pg < a.num_pages;
+        page = (uint32_t)pg;
+        slot = (uint32_t)pos - pidx * (uint32_t)a.page_size;
+      }
+    }
+    if (!ok) {
+      if (h == 0 && c == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
+      continue;
+    }
+    const KeyLoc loc{page, slot};
+    const uint64_t ko = key_offset(loc, a.k_s_page, a.k_s_tok, (uint32_t)h * a.k_s_head + c * 8);
+    const uint64_t vo = key_offset(loc, a.v_s_page, a.v_s_tok, (uint32_t)h * a.v_s_head + c * 8);
+    const int64_t ks = (t * a.ak_s_tok + (int64_t)h * a.ak_s_head + c * 8) * 2;
+    const int64_t vs = (t * a.av_s_tok + (int64_t)h * a.av_s_head + c * 8) * 2;
+    *reinterpret_cast<uint4*>(kp + ko * 2) = *reinterpret_cast<const uint4*>(ak + ks);
+    *reinterpret_cast<uint4*>(vp + vo * 2) = *reinterpret_cast<const uint4*>(av + vs);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <typename T, int D, int PM>
@@ -774,6 +823,14 @@ hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a, c
   if (dtype == 2)
     return launch_merge_t<float>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rh, head_dim, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t units = a.num_tokens * a.heads * (a.head_dim / 8);
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + 255) / 256 < 8192 ? (units + 255) / 256 : 8192;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s) {

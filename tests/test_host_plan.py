@@ -186,3 +186,30 @@ def test_verify_plan_is_causal_stride_k():
     b = pk.plan_host(qo, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 32, 8, 128, 16,
                      True).work_items()
     assert np.array_equal(a, b)
+
+
+def _append_call(lib, dtype=0, tokens=4, heads=2, dim=128, batch=1, k_page_size=16,
+                 v_page_size=16, k_pages=8, v_pages=8, ak_s_tok=256, k_s_tok=256, ptr=None):
+    # pointers are never dereferenced: every case here is refused (or empty) on the host
+    return lib.pkv_append_kv(ptr, ak_s_tok, 128, ptr, 256, 128, tokens, heads, dim,
+                             ptr, ptr, ptr, batch, ptr, 4,
+                             ptr, k_pages, k_page_size, 16 * 256, k_s_tok, 128,
+                             ptr, v_pages, v_page_size, 16 * 256, 256, 128,
+                             dtype, None, None)
+
+
+def test_append_refusals_on_host():
+    lib = pk.load_library()
+    assert _append_call(lib, tokens=0) == 0                       # nothing to write
+    assert _append_call(lib, dtype=2) == pk.PKV_EINVAL            # fp32 cache
+    assert _append_call(lib, dim=100) == pk.PKV_EINVAL
+    assert _append_call(lib, heads=0) == pk.PKV_EINVAL
+    assert _append_call(lib, tokens=-1) == pk.PKV_EINVAL
+    assert _append_call(lib, v_page_size=8) == pk.PKV_EMISMATCH
+    assert _append_call(lib, v_pages=9) == pk.PKV_EMISMATCH
+    assert _append_call(lib) == pk.PKV_EINVAL                     # NULL device pointers
+    assert b"NULL" in lib.pkv_last_error()
+    fake = 1 << 20                                                # aligned, never touched
+    assert _append_call(lib, ptr=fake, ak_s_tok=260) == pk.PKV_ELAYOUT
+    assert _append_call(lib, ptr=fake, k_s_tok=1 << 31) == pk.PKV_ELAYOUT
+    assert _append_call(lib, ptr=fake + 8) == pk.PKV_ELAYOUT      # misaligned
