@@ -180,11 +180,15 @@ pkv_status pkv_merge_states(const void* o_a, const float* lse_a, const void* o_b
 
 /*
  * append_kv: write new key/value rows into a paged cache, the step before an
- * attention call over the same page table (PR #399, Architecture notes: an
- * append writes scattered pages).  Token t belongs to request
- * batch_indices[t] at logical position positions[t] and lands on page
- * kv_page_indices[kv_indptr[b] + positions[t] / page_size], slot
- * positions[t] % page_size; K and V rows are copied bit for bit.
+ * attention call over the same page table (PR #399, per-commit messages, the
+ * torch.compile aliasing commit: an append writes scattered pages).  Token t
+ * belongs to request batch_indices[t] at logical position positions[t] and
+ * lands on page kv_page_indices[kv_indptr[b] + positions[t] / page_size],
+ * slot positions[t] % page_size; K and V rows are copied bit for bit.  The
+ * caller owns kv_last_page_len: a position may lie anywhere on the request's
+ * pages.  Two tokens naming one slot race (the surviving row is unspecified).
+ * The kernel runs on `stream` and, like every entry point, does not
+ * synchronise.
  *   append_k, append_v: [num_tokens, num_kv_heads, head_dim] device arrays
  *     (token / head strides in elements, head_dim packed).
  *   batch_indices, positions [num_tokens], kv_indptr [batch_size + 1],

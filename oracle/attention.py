@@ -294,8 +294,9 @@ def append_paged_kv(k_pool, v_pool, append_k, append_v, batch_indices, positions
 
     Token t belongs to request batch_indices[t] at logical position
     positions[t]; it lands on page kv_page_indices[kv_indptr[b] + pos // P],
-    slot pos % P (the same page table attention reads, PR #399's note that
-    appends write scattered pages).  Rows are copied exactly; every other slot
+    slot pos % P (the same page table attention reads; PR #399, per-commit
+    messages, the torch.compile aliasing commit: an append writes scattered
+    pages).  Rows are copied exactly; every other slot
     is left untouched.  append_k / append_v: [tokens, Hkv, D].
     """
     k_out = np.array(k_pool, copy=True)

@@ -451,7 +451,7 @@ def append_kv(append_k, append_v, batch_indices, positions, kv_indptr, kv_page_i
         if t.dim() != 3 or t.dtype != paged_k.dtype or t.device != dev:
             raise PkvError(PKV_EMISMATCH, f"{name}: expected a [tokens, heads, head_dim] "
                                           f"{paged_k.dtype} tensor on {dev}")
-        if t.stride(2) != 1:
+        if t.numel() and t.stride(2) != 1:   # empty tensors may carry any strides
             raise PkvError(PKV_ELAYOUT, f"{name}: head_dim stride must be 1")
         if tuple(t.shape) != (append_k.shape[0], k.shape[2], k.shape[3]):
             raise PkvError(PKV_EMISMATCH, f"{name}: expected [{append_k.shape[0]}, "

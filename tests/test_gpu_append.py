@@ -141,10 +141,10 @@ def test_attention_over_appended_cache(pk, window_left):
     tokens_b, tokens_pos, ks, vs = [], [], [], []
     for b in range(w.batch_size):
         L = int(w.kv_lens[b])
-        kb = oracle.gather_request_kv(w.k_pool, w.kv_indptr, w.kv_page_indices, b, L,
-                                      w.page_size)
-        vb = oracle.gather_request_kv(w.v_pool, w.kv_indptr, w.kv_page_indices, b, L,
-                                      w.page_size)
+        j = np.arange(L)
+        ids = w.kv_page_indices[int(w.kv_indptr[b]) + j // w.page_size]
+        kb = w.k_pool[ids, j % w.page_size]          # storage bits, not floats
+        vb = w.v_pool[ids, j % w.page_size]
         tokens_b += [b] * L
         tokens_pos += list(range(L))
         ks.append(kb)

@@ -166,8 +166,14 @@ def test_config5_split_kv(pk, qo_len, window_left):
     tensors = device_inputs(w)
     o8, lse8, p8 = run(pk, w, tensors, num_kv_chunks=W.CONFIG5_CHUNKS)
     # with the 4095-key window every visible key lies in the last 8192-key chunk:
-    # the empty chunks are dropped and nothing is split
-    assert (p8.info["num_merge_items"] > 0) == (window_left == -1)
+    # the empty chunks are dropped (that chunk may still be sub-split for parallelism)
+    chunk = 65536 // W.CONFIG5_CHUNKS
+    work = p8.work_items()
+    live = work[work[:, 3] > 0]
+    if window_left == -1:
+        assert p8.info["num_merge_items"] > 0 and (live[:, 4] < chunk).any()
+    else:
+        assert (live[:, 4] >= (W.CONFIG5_CHUNKS - 1) * chunk).all()
     check_sampled(w, o8, lse8, np.random.default_rng(5), f"config5 q={qo_len} w={window_left}",
                   floats=floats, per_request=2, heads=3)
     oa, lsea, _ = run(pk, w, tensors)   # scheduler's own split
@@ -175,7 +181,6 @@ def test_config5_split_kv(pk, qo_len, window_left):
     assert np.abs(lsea - lse8).max() <= 1e-3
     # the same 8 chunks as separate partial states, folded with merge_states
     q, k, v = tensors
-    chunk = 65536 // W.CONFIG5_CHUNKS
     acc_o = acc_l = None
     for c in range(W.CONFIG5_CHUNKS):
         p = plan_for(pk, w, kv_begin=c * chunk, kv_end=(c + 1) * chunk)
