@@ -165,7 +165,13 @@ def _random_pools(w, dev, copies, seed):
 
 
 def time_rotating(p, q, pools, iters, warmup=2):
-    """Average run() time (ms) from HIP events, cycling through K/V pool copies."""
+    """Average run() time (ms) from HIP events, cycling through K/V pool copies.
+
+    Returns (eager, graph): eager brackets each run() call on the stream, so it
+    includes the host's per-call cost whenever that exceeds the kernels'; graph
+    replays one captured HIP graph holding one run() per pool copy and divides
+    by the copies, which is the device time of the launches alone (run() makes
+    no allocation, copy or synchronisation, so it can be captured)."""
     import torch
     s = torch.cuda.current_stream()
     o = torch.empty((p.total_q_rows, p.num_qo_heads, p.head_dim), dtype=p.dtype, device=q.device)
@@ -181,7 +187,24 @@ def time_rotating(p, q, pools, iters, warmup=2):
         p.run(q, k, v, out=o, lse=lse)
         b.record(s)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    eager = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k, v in pools:
+            p.run(q, k, v, out=o, lse=lse)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, iters // len(pools))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(s)
+        g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    graph = float(np.mean([a.elapsed_time(b) for a, b in evs])) / len(pools)
+    del g
+    return eager, graph
 
 
 def coverage(pk, torch, dev, iters=20):
@@ -213,11 +236,11 @@ def coverage(pk, torch, dev, iters=20):
         copies = max(1, min(16, -(-512_000_000 // max(nbytes, 1))))
         q, pools = _random_pools(w, dev, copies, seed=7000 + i)
         p = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
-        ms = time_rotating(p, q, pools, iters)
+        eager_ms, ms = time_rotating(p, q, pools, iters)
         flops = attention_flops(w)
         # the roofline that binds: arithmetic intensity against the ridge point
         hbm_bound = flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        rec = {"workload": name, "ms": ms, "TFLOP/s": flops / ms / 1e9,
+        rec = {"workload": name, "ms": ms, "eager_ms": eager_ms, "TFLOP/s": flops / ms / 1e9,
                "GB/s": nbytes / ms / 1e6, "bound": "hbm" if hbm_bound else "mfma",
                "pool_copies": copies, "work_items": p.info["num_work_items"],
                "split_tiles": p.info["num_merge_items"]}
@@ -259,14 +282,22 @@ def time_append(pk, torch, dev, name, w, per_req, iters):
     s = torch.cuda.current_stream()
     for i in range(2):
         pk.append_kv(*srcs[i % copies], bi, pos, indptr, pages, k, v)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()       # device time of the launches (see time_rotating)
+    with torch.cuda.graph(g):
+        for src in srcs:
+            pk.append_kv(*src, bi, pos, indptr, pages, k, v)
+    g.replay()
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    for i, (a, b) in enumerate(evs):
+           for _ in range(max(2, iters // copies))]
+    for a, b in evs:
         a.record(s)
-        pk.append_kv(*srcs[i % copies], bi, pos, indptr, pages, k, v)
+        g.replay()
         b.record(s)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / copies
+    del g
     rec = {"workload": name, "ms": ms, "GB/s": nbytes / ms / 1e6, "bound": "hbm",
            "tokens": tokens, "source_copies": copies}
     rec["frac"] = rec["GB/s"] / PEAK_HBM_GBS

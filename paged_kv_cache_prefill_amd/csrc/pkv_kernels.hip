@@ -36,118 +36,23 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLn2 = 0.693147180559945309417f;
-constexpr float kTau = 8.f;   // lazy-rescale threshold, log2 units
-constexpr float kNegInf = -__builtin_inff();
-
-template <typename T>
-struct Traits;
-
-template <>
-struct Traits<__bf16> {
-  typedef bf16x8 frag;
-  static __device__ __forceinline__ f32x4 mfma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Traits<_Float16> {
-  typedef f16x8 frag;
-  static __device__ __forceinline__ f32x4 mfma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <typename T>
-__device__ __forceinline__ float to_f32(T x) {
-  return static_cast<float>(x);
-}
-
-template <typename T>
-__device__ __forceinline__ T from_f32(float x) {
-  return static_cast<T>(x);  // round to nearest even
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-
-// Page-table address path, shared by the attention and debug-gather kernels:
-// logical key j of a request lives on page ptab[j / P] at slot j % P, and
-// element e of head h of that key at page * s_page + slot * s_tok + h * s_head + e.
-struct KeyLoc {
-  uint32_t page, slot;
-};
-__device__ __forceinline__ KeyLoc locate_key(const int32_t* ptab, uint32_t j, uint32_t magic,
-                                             uint32_t shift, uint32_t page_size) {
-  const uint32_t pidx = (uint32_t)(((uint64_t)j * magic) >> shift);
-  return KeyLoc{(uint32_t)ptab[pidx], j - pidx * page_size};
-}
-__device__ __forceinline__ uint64_t key_offset(KeyLoc k, uint32_t s_page, uint32_t s_tok,
-                                               uint32_t in_page) {
-  return (uint64_t)k.page * s_page + (k.slot * s_tok + in_page);
-}
-
-// ---------------------------------------------------------------------------
-// attention
-// ---------------------------------------------------------------------------
-// LDS tiles hold key rows of D elements as CH = D/8 16-byte chunks,
-// row-major and unpadded, with the chunk order permuted per row so that the
-// reads of one MFMA fragment spread over all banks:
-//  * K (16-byte reads, consecutive lanes on consecutive rows, same chunk):
-//    chunk c of row r sits at position c ^ (r & 15) (r & 7 when CH = 8);
-//  * V (transposing 8-byte reads: 16 lanes cover 4 consecutive keys x 2
-//    adjacent chunks): chunk c of key k sits at c ^ ((2k) & (CH - 1)), which
-//    keeps those 8 chunks, and 32 lanes' 16, on distinct positions.
-template <int CH>
-__device__ __forceinline__ int swz_k(int row, int chunk) {
-  return chunk ^ (row & (CH >= 16 ? 15 : 7));
-}
-template <int CH>
-__device__ __forceinline__ int swz_v(int key, int chunk) {
-  return chunk ^ ((2 * key) & (CH - 1));
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// 16 bytes from global memory straight into LDS: lane i of the wave writes
-// dst + 16 * i (dst is wave-uniform).
-__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-// Wait for every outstanding memory operation of this wave.
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
-// Two transposing 8-byte LDS reads joined into one 8-element fragment.
-__device__ __forceinline__ i16x8 lds_read_tr16_x2(const char* p0, const char* p1) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ bool wave_any(bool x) { return __any(x); }
-
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
-};
 
 // WM waves split the rows, WN waves split the keys of each LDS tile;
 // each wave owns QB blocks of 16 rows and NW keys of the tile.  WPE is the
 // number of waves per SIMD the register budget is sized for.  PM selects the
-// page addressing of complete key tiles: 0 any page size (per-key page-table
-// lookup), 1 power-of-two pages no longer than the tile (each lane's slot is
-// fixed), 2 power-of-two pages at least as long as the tile (one page per
-// tile).  The last, partial tile of a task always takes the general path.
+// page addressing: 0 any page size (per-key page-table lookup), 1 power-of-
+// two pages shorter than one load instruction's rows (each lane's slot is
+// fixed on complete tiles), 3 power-of-two pages of at least one load
+// instruction's rows: each instruction stays on one page, so its page id is
+// a scalar load and its address an SGPR base plus a per-lane 32-bit offset,
+// issued from assembly (dma16), which the compiler does not track; the
+// wait-all and barrier closing every tile make those loads visible.  With PM
+// 0 and 1 the last, partial tile of a task takes the general path.
 template <typename T, int D, int WM, int WN, int QB, int NW, int WPE, int PM>
 __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   using Tr = Traits<T>;
@@ -246,35 +151,41 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // Direct global->LDS loads: wave instruction m fills tile slots
   // [(m * NWAVE + wave) * 64, +64); lane i writes slot +i, which is key row
   // (m * NWAVE + wave) * RPI + i / CH at position i % CH, i.e. logical chunk
-  // (i % CH) ^ (row & 7).  Keys at or past kv_end read the last key instead
+  // swz_k / swz_v of it.  Keys at or past kv_end read the last key instead
   // (finite data, masked to zero weight), so no read leaves the request.
   uint32_t koff[NI], voff[NI];   // element offsets of this lane's chunks within a key row
-  uint32_t kin[NI], vin[NI];     // ... plus the lane's fixed slot (PM 1) or row (PM 2)
+  uint32_t kin[NI], vin[NI];     // ... plus the lane's fixed slot (PM 1) or row (PM 3)
   int lrow[NI];
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
     lrow[m] = (m * NWAVE + wave) * RPI + lane / CH;
     koff[m] = (uint32_t)swz_k<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.k_s_head;
     voff[m] = (uint32_t)swz_v<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.v_s_head;
-    const uint32_t lslot = (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
+    const uint32_t lslot = PM == 3 ? (uint32_t)(lane / CH)
+                                   : (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
     kin[m] = lslot * a.k_s_tok + koff[m];
     vin[m] = lslot * a.v_s_tok + voff[m];
   }
   // page (and, on the general path, slot) of each lane row of the next tile
   uint32_t lpage[NI], lslot[NI];
-  uint32_t tile_page = 0;   // PM 2: the next tile's single page
+  uint32_t spage[NI];       // PM 3: page of each load instruction's rows (scalar)
   const int32_t* ptab = a.pages + rq.page_off;
+  const const_i32* ptab_s = (const const_i32*)ptab;   // scalar loads
   auto fetch_pages = [&](int j0) {
-    const bool fast = PM != 0 && j0 + NWG <= it.kv_end;
-    if (PM == 1 && fast) {
+    if constexpr (PM == 3) {
+#pragma unroll
+      for (int m = 0; m < NI; ++m)
+        spage[m] = (uint32_t)ptab_s[(uint32_t)min(j0 + (m * NWAVE + wave) * RPI, last_key) >>
+                                    a.page_shift];
+      return;
+    }
+    if (PM == 1 && j0 + NWG <= it.kv_end) {
       const int32_t* pt = ptab + (j0 >> a.page_shift);
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
         lpage[m] = (uint32_t)pt[lrow[m] >> a.page_shift];
         lslot[m] = (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
       }
-    } else if (PM == 2 && fast) {
-      tile_page = (uint32_t)ptab[j0 >> a.page_shift];
     } else {
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
@@ -286,14 +197,34 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
   };
   auto issue_tile = [&](int j0, uint4* kdst, uint4* vdst) {
-    if (PM != 0 && j0 + NWG <= it.kv_end) {
-      const uint32_t slot0 = (uint32_t)j0 & (uint32_t)(a.page_size - 1);
-      const uint64_t kt0 = (uint64_t)tile_page * a.k_s_page + slot0 * a.k_s_tok;
-      const uint64_t vt0 = (uint64_t)tile_page * a.v_s_page + slot0 * a.v_s_tok;
+    if constexpr (PM == 3) {
+      // one page per instruction: SGPR base + per-lane 32-bit byte offset
+      const char* kb = reinterpret_cast<const char*>(kp);
+      const char* vb = reinterpret_cast<const char*>(vp);
+      const uint32_t lk = (uint32_t)(uintptr_t)kdst, lv = (uint32_t)(uintptr_t)vdst;
+      const uint32_t pmask = (uint32_t)a.page_size - 1;
+      const bool full = j0 + NWG <= it.kv_end;
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const uint64_t ko = PM == 1 ? (uint64_t)lpage[m] * a.k_s_page + kin[m] : kt0 + kin[m];
-        const uint64_t vo = PM == 1 ? (uint64_t)lpage[m] * a.v_s_page + vin[m] : vt0 + vin[m];
+        const int rk = j0 + (m * NWAVE + wave) * RPI;
+        const uint32_t lofs = (uint32_t)((m * NWAVE + wave) * 64 * 16);
+        const char* kpg = kb + (uint64_t)spage[m] * a.k_s_page * sizeof(T);
+        const char* vpg = vb + (uint64_t)spage[m] * a.v_s_page * sizeof(T);
+        if (full) {
+          const uint32_t slot0 = (uint32_t)rk & pmask;
+          dma16(kpg + slot0 * a.k_s_tok * sizeof(T), kin[m] * sizeof(T), lk + lofs);
+          dma16(vpg + slot0 * a.v_s_tok * sizeof(T), vin[m] * sizeof(T), lv + lofs);
+        } else {
+          const uint32_t slot = (uint32_t)min(rk + lane / CH, last_key) & pmask;
+          dma16(kpg, (slot * a.k_s_tok + koff[m]) * sizeof(T), lk + lofs);
+          dma16(vpg, (slot * a.v_s_tok + voff[m]) * sizeof(T), lv + lofs);
+        }
+      }
+    } else if (PM == 1 && j0 + NWG <= it.kv_end) {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const uint64_t ko = (uint64_t)lpage[m] * a.k_s_page + kin[m];
+        const uint64_t vo = (uint64_t)lpage[m] * a.v_s_page + vin[m];
         const int base = (m * NWAVE + wave) * 64;
         load_lds16(kp + ko, kdst + base);
         load_lds16(vp + vo, vdst + base);
@@ -763,8 +694,8 @@ static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream
   if (a.num_work == 0) return hipSuccess;
   const int nwg = tile_keys(tile_kind);
   const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
-  if (pow2 && a.page_size <= nwg) return launch_attention_pm<T, D, 1>(tile_kind, a, s);
-  if (pow2) return launch_attention_pm<T, D, 2>(tile_kind, a, s);
+  if (pow2 && a.page_size >= 512 / D) return launch_attention_pm<T, D, 3>(tile_kind, a, s);
+  if (pow2) return launch_attention_pm<T, D, 1>(tile_kind, a, s);
   return launch_attention_pm<T, D, 0>(tile_kind, a, s);
 }
 

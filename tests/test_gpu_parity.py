@@ -96,6 +96,29 @@ def test_ragged_tails_and_empty_requests(pk):
         assert_close(o, lse, ref_o, ref_lse, w.dtype, f"ragged tile={tile}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("page", [4, 8, 32, 64, 128, 1024])
+def test_prefill_kernels_across_page_sizes(pk, d, page):
+    """Both tile shapes over every power-of-two page address path (pages that
+    hold part of a load instruction's rows, a few instructions' rows, several
+    pages per key tile, one page per tile), key runs of one, two, three and
+    many tiles, ragged tails, windows, and split chunks writing partials."""
+    rng = np.random.default_rng(page * 1000 + d)
+    qo = [1, 20, 50, 130, 3]
+    kv = [1, 45, 96, 700, 33]
+    for causal, w in ((True, -1), (True, 40), (False, 17), (False, -1)):
+        wl = W.build("pages", qo, kv, 8, 2, d, page, causal, w, W.BF16,
+                     seed=int(rng.integers(1 << 30)), poison=True)
+        ref_o, ref_lse = oracle_full(wl)
+        tensors = device_inputs(wl)
+        for tile in (1, 2):
+            for chunks in (0, 3):
+                o, lse, _ = run(pk, wl, tensors, tile=tile, num_kv_chunks=chunks)
+                assert_close(o, lse, ref_o, ref_lse, wl.dtype,
+                             f"pages P={page} d={d} causal={causal} w={w} tile={tile} "
+                             f"chunks={chunks}")
+
+
 def test_empty_batch(pk):
     p = pk.plan([0], [0], [], [], 4, 2, 64, 16, True, dtype=torch.float16)
     q = torch.zeros((0, 4, 64), dtype=torch.float16, device="cuda")
