@@ -505,41 +505,57 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// merge of split-KV partial states (N-way), one work group per split tile
+// merge of split-KV partial states (N-way), work groups of rows of one split tile
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
+  // TPR threads own one row (4 head-dim elements each); a work group covers
+  // RPW rows of one split query tile.  The threads of a row split the slots
+  // for the max and the weight sum (reduced with shuffles inside the row's
+  // TPR-lane group), then every thread sweeps all slots for its 4 elements,
+  // the slot weights broadcast from the thread that computed them; the
+  // partial-o loads of different slots are independent, so they overlap.
+  constexpr int TPR = D / 4;
+  constexpr int RPW = 256 / TPR;
   const MergeItem it = a.items[blockIdx.x];
+  const int rl = blockIdx.y * RPW + (int)threadIdx.x / TPR;
+  const int d4 = (int)threadIdx.x % TPR;
+  if (rl >= it.nrows) return;                     // whole TPR-lane groups leave together
   const ReqInfo rq = a.reqs[it.b];
   const int G = a.group;
-  T* __restrict__ op = static_cast<T*>(a.o);
-  for (int idx = threadIdx.x; idx < it.nrows * (D / 4); idx += blockDim.x) {
-    const int rl = idx / (D / 4);
-    const int d4 = idx - rl * (D / 4);
-    float mt = kNegInf;
-    for (int c = 0; c < it.nslots; ++c)
-      mt = fmaxf(mt, a.part_lse[(int64_t)(it.slot0 + c) * a.tile_rows + rl]);
-    const float mu = (mt == kNegInf) ? 0.f : mt;
-    float wt = 0.f;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < it.nslots; ++c) {
-      const int64_t sr = (int64_t)(it.slot0 + c) * a.tile_rows + rl;
-      const float w = fast_exp2(a.part_lse[sr] - mu);
-      wt += w;
-      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + sr * D + d4 * 4);
-    }
-    const float inv = wt > 0.f ? 1.f / wt : 0.f;
-    const int r = it.row0 + rl;
-    const int pos = r / G;
-    const int h = it.kvh * G + (r - pos * G);
-    const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
-    T o4[4];
+  const int64_t tr = a.tile_rows;
+  const float* lse = a.part_lse + (int64_t)it.slot0 * tr + rl;   // slot c at lse[c * tr]
+  const float* po = a.part_o + ((int64_t)it.slot0 * tr + rl) * D + d4 * 4;
+  float mt = kNegInf;
+  for (int c = d4; c < it.nslots; c += TPR) mt = fmaxf(mt, lse[c * tr]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i] * inv);
-    *reinterpret_cast<uint2*>(op + orow * D + d4 * 4) = *reinterpret_cast<uint2*>(o4);
-    if (d4 == 0 && a.lse != nullptr)
-      a.lse[orow] = (mt == kNegInf) ? kNegInf : (mt + fast_log2(wt)) * kLn2;
+  for (int o = TPR / 2; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, TPR));
+  const float mu = (mt == kNegInf) ? 0.f : mt;
+  float wt = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < it.nslots; c0 += TPR) {
+    const float mw = c0 + d4 < it.nslots ? fast_exp2(lse[(c0 + d4) * tr] - mu) : 0.f;
+    wt += mw;
+    const int cnt = min(TPR, it.nslots - c0);
+    for (int j = 0; j < cnt; ++j) {
+      const float w = __shfl(mw, j, TPR);
+      acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)(c0 + j) * tr * D);
+    }
   }
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) wt += __shfl_xor(wt, o, TPR);
+  const float inv = wt > 0.f ? 1.f / wt : 0.f;
+  const int r = it.row0 + rl;
+  const int pos = r / G;
+  const int h = it.kvh * G + (r - pos * G);
+  const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+  T o4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i] * inv);
+  T* __restrict__ op = static_cast<T*>(a.o);
+  *reinterpret_cast<uint2*>(op + orow * D + d4 * 4) = *reinterpret_cast<uint2*>(o4);
+  if (d4 == 0 && a.lse != nullptr)
+    a.lse[orow] = (mt == kNegInf) ? kNegInf : (mt + fast_log2(wt)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -710,7 +726,8 @@ hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnAr
 
 hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a, hipStream_t s) {
   if (a.num_items == 0) return hipSuccess;
-  dim3 grid(a.num_items);
+  const int rpw = 256 / (head_dim / 4);   // rows per work group
+  dim3 grid(a.num_items, (a.tile_rows + rpw - 1) / rpw);
   if (dtype == 1 && head_dim == 128)
     hipLaunchKernelGGL((split_merge_kernel<__bf16, 128>), grid, dim3(256), 0, s, a);
   else if (dtype == 1 && head_dim == 64)
