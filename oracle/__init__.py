@@ -3,8 +3,10 @@
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the library.  See attention.py.
 """
-from .attention import (NEG_INF, allowed_mask, append_paged_kv, attention, attention_bruteforce, attention_rows,
+from .attention import (NEG_INF, allowed_mask, append_paged_kv, attention,
+                        attention_bruteforce, attention_rows, custom_mask_rows,
                         gather_request_kv, kv_lengths, merge_many, merge_states)
 
-__all__ = ["NEG_INF", "allowed_mask", "append_paged_kv", "attention", "attention_bruteforce", "attention_rows",
-           "gather_request_kv", "kv_lengths", "merge_many", "merge_states"]
+__all__ = ["NEG_INF", "allowed_mask", "append_paged_kv", "attention", "attention_bruteforce",
+           "attention_rows", "custom_mask_rows", "gather_request_kv", "kv_lengths",
+           "merge_many", "merge_states"]

@@ -15,6 +15,7 @@ matmul / exp / log as the only library steps:
 * ``attention_bruteforce`` -- the same definition as per-element Python loops.
 * ``merge_states`` / ``merge_many`` -- combining partial (o, lse) states.
 * ``append_paged_kv``   -- writing new K/V rows into their pages.
+* ``custom_mask_rows``  -- a request's topology mask (tree drafts) from packed bits.
 
 Sources (web pages of the AMD-Ecosystem FlashInfer fork):
   [W]  PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
@@ -30,6 +31,8 @@ Sources (web pages of the AMD-Ecosystem FlashInfer fork):
        wrongly", What changed / GQA head divisibility.
   [M]  PR #399, What changed / Graph-mode partial_state merge, and PR #362's
        split-KV test commit (partial (o, lse) states merged into one result).
+  [T]  PR #362, Architecture / design notes: a causal mask verifies chain
+       drafts only; tree drafts need a topology mask (custom_mask).
 
 Readings where the pages are silent (each also listed in the design notes):
   * kv_len = (n_pages - 1) * page_size + last_page_len, 0 for no pages.
@@ -39,7 +42,12 @@ Readings where the pages are silent (each also listed in the design notes):
   * GQA: q head h reads kv head h // (Hq // Hkv) (consecutive groups).
   * lse uses the natural logarithm.
   * a row with no visible key has o = 0 and lse = -inf (only reachable for a
-    partial state restricted to a key range).
+    partial state restricted to a key range, or a custom mask).
+  * custom mask [T]: request b's mask is the row-major [qo_len, kv_len]
+    boolean matrix (query i, key j) -> bit i * kv_len + j, packed
+    little-endian (bit k sits in byte k // 8 at bit k % 8) from byte
+    mask_indptr[b].  It replaces the causal mask (causal must be off); the
+    left window still applies on top of it.
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (brute force, closed forms, library routines, invariants, golden fixtures).
 """
@@ -104,6 +112,32 @@ def allowed_mask(qo_len, kv_len, causal, window_left, kv_begin=None, kv_end=None
     return ok
 
 
+def custom_mask_rows(custom_mask, mask_indptr, b, qo_len, kv_len):
+    """Boolean [qo_len, kv_len] topology mask of request b from packed bits [T].
+
+    Bit i * kv_len + j (little-endian within each byte, request b's bits from
+    byte mask_indptr[b]) says whether query row i may attend key j.
+    """
+    start = int(mask_indptr[b])
+    n = int(qo_len) * int(kv_len)
+    nbytes = (n + 7) // 8
+    seg = np.asarray(custom_mask[start:start + nbytes], dtype=np.uint8)
+    if seg.size != nbytes:
+        raise ValueError(f"custom_mask: request {b} needs {nbytes} bytes from {start}")
+    bits = np.unpackbits(seg, bitorder="little")[:n]
+    return bits.reshape(int(qo_len), int(kv_len)).astype(bool)
+
+
+def _check_custom(custom_mask, mask_indptr, causal):
+    if custom_mask is None:
+        return False
+    if mask_indptr is None:
+        raise ValueError("custom_mask needs mask_indptr")
+    if causal:
+        raise ValueError("a custom mask replaces the causal mask: pass causal=False")
+    return True
+
+
 def _check_heads(num_qo_heads, num_kv_heads):
     # [G]: a group size that does not divide the head count is refused.
     if num_kv_heads <= 0 or num_qo_heads % num_kv_heads != 0:
@@ -112,7 +146,8 @@ def _check_heads(num_qo_heads, num_kv_heads):
 
 def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
               kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
-              window_left, sm_scale, kv_begin=None, kv_end=None):
+              window_left, sm_scale, kv_begin=None, kv_end=None, custom_mask=None,
+              mask_indptr=None):
     """Masked softmax attention over a paged KV cache, in float64.
 
     q: [total_q, Hq, D]; k_pool, v_pool: NHD [num_pages, P, Hkv, D].
@@ -124,8 +159,11 @@ def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
     A row with no allowed key gets o = 0, lse = -inf.
     kv_begin/kv_end (optional) restrict every request to keys in that range of
     its own key coordinates, giving the partial state of one KV chunk.
+    custom_mask/mask_indptr (optional, packed bits [T]) intersect the mask with
+    each request's topology mask.
     """
     _check_heads(num_qo_heads, num_kv_heads)
+    use_custom = _check_custom(custom_mask, mask_indptr, causal)
     group = num_qo_heads // num_kv_heads
     q = np.asarray(q, dtype=np.float64)
     total_q, hq, d = q.shape
@@ -141,6 +179,8 @@ def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
         kb = gather_request_kv(k_pool, kv_indptr, kv_page_indices, b, L, page_size)
         vb = gather_request_kv(v_pool, kv_indptr, kv_page_indices, b, L, page_size)
         mask = allowed_mask(qo_len, L, causal, window_left, kv_begin, kv_end)
+        if use_custom:
+            mask = mask & custom_mask_rows(custom_mask, mask_indptr, b, qo_len, L)
         has_key = mask.any(axis=1)
         for h in range(hq):
             g = h // group
@@ -159,7 +199,8 @@ def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
 
 def attention_bruteforce(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
                          kv_last_page_len, num_qo_heads, num_kv_heads, page_size,
-                         causal, window_left, sm_scale, kv_begin=None, kv_end=None):
+                         causal, window_left, sm_scale, kv_begin=None, kv_end=None,
+                         custom_mask=None, mask_indptr=None):
     """The same definition as ``attention`` as literal per-element loops.
 
     Pure Python floats (IEEE double), no NumPy arithmetic: for tiny inputs only.
@@ -167,6 +208,7 @@ def attention_bruteforce(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indice
     evaluated per (request, head, row, key).
     """
     _check_heads(num_qo_heads, num_kv_heads)
+    use_custom = _check_custom(custom_mask, mask_indptr, causal)
     group = num_qo_heads // num_kv_heads
     total_q, hq, d = np.shape(q)
     o = [[[0.0] * d for _ in range(hq)] for _ in range(total_q)]
@@ -191,6 +233,11 @@ def attention_bruteforce(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indice
                         ok = False
                     if kv_end is not None and j >= kv_end:
                         ok = False
+                    if use_custom:
+                        bit = i * L + j
+                        byte = int(custom_mask[int(mask_indptr[b]) + bit // 8])
+                        if (byte >> (bit % 8)) & 1 == 0:
+                            ok = False
                     if not ok:
                         continue
                     page = int(kv_page_indices[int(kv_indptr[b]) + j // page_size])
@@ -252,7 +299,8 @@ def merge_many(os, lses):
 
 def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
                    kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
-                   window_left, sm_scale, b, rows, heads, kv_begin=None, kv_end=None):
+                   window_left, sm_scale, b, rows, heads, kv_begin=None, kv_end=None,
+                   custom_mask=None, mask_indptr=None):
     """``attention`` restricted to some rows and q heads of request b.
 
     Same definition, float64; used to check full-size workloads on sampled
@@ -261,6 +309,7 @@ def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
     The request's keys are read page by page through its page table.
     """
     _check_heads(num_qo_heads, num_kv_heads)
+    use_custom = _check_custom(custom_mask, mask_indptr, causal)
     group = num_qo_heads // num_kv_heads
     L = int(kv_lengths(kv_indptr, kv_last_page_len, page_size)[b])
     q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
@@ -268,6 +317,8 @@ def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
     first, n_pages = int(kv_indptr[b]), int(kv_indptr[b + 1]) - int(kv_indptr[b])
     pages = np.asarray(kv_page_indices[first:first + n_pages], dtype=np.int64)
     mask = allowed_mask(qo_len, L, causal, window_left, kv_begin, kv_end)
+    if use_custom:
+        mask = mask & custom_mask_rows(custom_mask, mask_indptr, b, qo_len, L)
     d = np.shape(q)[2]
     o = np.zeros((len(rows), len(heads), d), dtype=np.float64)
     lse = np.full((len(rows), len(heads)), NEG_INF, dtype=np.float64)

@@ -19,6 +19,7 @@ import torch
 
 import oracle
 import workloads
+import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -513,3 +514,121 @@ def test_append_then_gather_round_trip():
         page = prob["kv_page_indices"][prob["kv_indptr"][b] + pos[t] // 16]
         touched[page, pos[t] % 16] = True
     np.testing.assert_array_equal(k[~touched], prob["k_pool"][~touched])
+
+
+# ---------------------------------------------------------------------------
+# custom (tree-draft topology) masks
+# ---------------------------------------------------------------------------
+def _tree_golden():
+    with open(os.path.join(GOLDEN, "tree_mask.json")) as f:
+        return json.load(f)
+
+
+def test_custom_mask_golden_bits():
+    g = _tree_golden()
+    want = np.array(g["mask"], dtype=bool)
+    got = oracle.custom_mask_rows(np.array(g["packed_bytes"], np.uint8), [0, 3], 0,
+                                  g["qo_len"], g["kv_len"])
+    assert np.array_equal(got, want)
+    # the input encoder used by the tests agrees with the hand-packed bytes
+    data, indptr = W.pack_custom_mask([W.tree_topology_mask(g["prefix_len"], g["parents"])])
+    assert list(data) == g["packed_bytes"] and list(indptr) == [0, 3]
+
+
+def test_custom_mask_golden_attention():
+    """K = 0 makes every visible score equal: lse = log(#visible) and o = the
+    mean of the visible V rows (V row j = j)."""
+    g = _tree_golden()
+    Q, L = g["qo_len"], g["kv_len"]
+    q = np.ones((Q, 1, 1))
+    k = np.zeros((2, 4, 1, 1))                       # two pages of 4 keys
+    v = np.arange(8, dtype=np.float64).reshape(2, 4, 1, 1)
+    o, lse = oracle.attention(q, k, v, [0, Q], [0, 2], [0, 1], [2], 1, 1, 4, False, -1, 1.0,
+                              custom_mask=np.array(g["packed_bytes"], np.uint8),
+                              mask_indptr=[0, 3])
+    assert np.allclose(lse[:, 0], np.log(g["visible_counts"]), atol=1e-12)
+    assert np.allclose(o[:, 0, 0], g["mean_of_key_index"], atol=1e-12)
+
+
+def _tree_case(rng, qo_trees, prefixes, hq, hkv, d, page, window):
+    mats = [W.tree_topology_mask(p, W.random_tree_parents(rng, n))
+            for n, p in zip(qo_trees, prefixes)]
+    kv = [p + n for n, p in zip(qo_trees, prefixes)]
+    w = W.build("tree", qo_trees, kv, hq, hkv, d, page, False, window, W.FP16,
+                seed=int(rng.integers(1 << 30)))
+    w.custom_mask, w.mask_indptr = W.pack_custom_mask(mats)
+    return w, mats
+
+
+def test_custom_mask_matches_bruteforce():
+    rng = np.random.default_rng(61)
+    for trial in range(6):
+        w, _ = _tree_case(rng, [int(x) for x in rng.integers(1, 7, size=2)],
+                          [int(x) for x in rng.integers(0, 9, size=2)], 4, 2, 8,
+                          int(rng.choice([1, 3, 4])), int(rng.choice([-1, 0, 2, 5])))
+        q, k, v = w.float_inputs()
+        a = w.plan_args()
+        del a["head_dim"]
+        o1, l1 = oracle.attention(q, k, v, **a)
+        o2, l2 = oracle.attention_bruteforce(q, k, v, **a)
+        assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+
+
+def test_custom_mask_reduces_to_causal_and_full():
+    rng = np.random.default_rng(62)
+    w = W.build("m", [5, 3], [9, 3], 4, 2, 8, 4, True, -1, W.FP16, seed=63)
+    q, k, v = w.float_inputs()
+    a = w.plan_args()
+    del a["head_dim"]
+    ref_c = oracle.attention(q, k, v, **a)
+    a_nc = {**a, "causal": False}
+    ref_n = oracle.attention(q, k, v, **a_nc)
+    causal_mats = [oracle.allowed_mask(int(ql), int(kl), True, -1)
+                   for ql, kl in zip(w.qo_lens, w.kv_lens)]
+    data, ind = W.pack_custom_mask(causal_mats)
+    got_c = oracle.attention(q, k, v, **a_nc, custom_mask=data, mask_indptr=ind)
+    data, ind = W.pack_custom_mask([np.ones((int(ql), int(kl)), bool)
+                                    for ql, kl in zip(w.qo_lens, w.kv_lens)])
+    got_n = oracle.attention(q, k, v, **a_nc, custom_mask=data, mask_indptr=ind)
+    for (o1, l1), (o2, l2) in ((ref_c, got_c), (ref_n, got_n)):
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # a chain (each node's parent is the previous one) is exactly causal verify
+    mats = [W.tree_topology_mask(int(kl) - int(ql), np.arange(int(ql)) - 1)
+            for ql, kl in zip(w.qo_lens, w.kv_lens)]
+    data, ind = W.pack_custom_mask(mats)
+    got = oracle.attention(q, k, v, **a_nc, custom_mask=data, mask_indptr=ind)
+    assert np.array_equal(got[0], ref_c[0]) and np.array_equal(got[1], ref_c[1])
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, **a, custom_mask=data, mask_indptr=ind)
+
+
+def test_custom_mask_tree_differs_from_causal():
+    """Non-vacuity: a branching tree must not give the causal answer (a causal
+    mask lets a draft token see its sibling branch)."""
+    rng = np.random.default_rng(64)
+    w, mats = _tree_case(rng, [6], [5], 2, 1, 8, 4, -1)
+    parents_branch = W.tree_topology_mask(5, [-1, 0, 0, 1, 1, 2])
+    w.custom_mask, w.mask_indptr = W.pack_custom_mask([parents_branch])
+    q, k, v = w.float_inputs()
+    a = w.plan_args()
+    del a["head_dim"]
+    o_t, _ = oracle.attention(q, k, v, **a)
+    a_c = {x: y for x, y in a.items() if x not in ("custom_mask", "mask_indptr")}
+    o_c, _ = oracle.attention(q, k, v, **{**a_c, "causal": True})
+    assert np.abs(o_t - o_c).max() > 0.1
+
+
+def test_custom_mask_rows_match_full():
+    rng = np.random.default_rng(65)
+    w, _ = _tree_case(rng, [7, 4, 9], [40, 3, 70], 8, 2, 16, 16, 30)
+    q, k, v = w.float_inputs()
+    a = w.plan_args()
+    del a["head_dim"]
+    o, lse = oracle.attention(q, k, v, **a)
+    for b in range(3):
+        rows = list(range(int(w.qo_lens[b])))
+        heads = [0, 5, 7]
+        o_r, l_r = oracle.attention_rows(q, k, v, **a, b=b, rows=rows, heads=heads)
+        q0 = int(w.qo_indptr[b])
+        assert np.allclose(o_r, o[q0:q0 + len(rows)][:, heads], atol=1e-12)
+        assert np.allclose(l_r, lse[q0:q0 + len(rows)][:, heads], atol=1e-12)

@@ -83,6 +83,8 @@ class Workload:
     q: np.ndarray = None       # storage arrays (int16 bf16 bits or float16)
     k_pool: np.ndarray = None
     v_pool: np.ndarray = None
+    custom_mask: np.ndarray = None   # packed topology bits (uint8) and their
+    mask_indptr: np.ndarray = None   # per-request byte offsets, or None
 
     @property
     def batch_size(self):
@@ -99,7 +101,9 @@ class Workload:
                     num_qo_heads=self.num_qo_heads, num_kv_heads=self.num_kv_heads,
                     head_dim=self.head_dim, page_size=self.page_size,
                     causal=self.causal, window_left=self.window_left,
-                    sm_scale=self.sm_scale)
+                    sm_scale=self.sm_scale,
+                    **({} if self.custom_mask is None else
+                       dict(custom_mask=self.custom_mask, mask_indptr=self.mask_indptr)))
 
     def float_inputs(self):
         return (to_float(self.q, self.dtype), to_float(self.k_pool, self.dtype),
@@ -216,3 +220,54 @@ def config5(variant=0, qo_len=64, window_left=-1, **kw):
 
 
 CONFIG5_CHUNKS = 8
+
+
+# ----------------------------------------------------------------------------
+# Tree drafts: topology masks (input encoding only; no attention arithmetic)
+# ----------------------------------------------------------------------------
+
+def pack_custom_mask(mats):
+    """Pack per-request boolean [qo_len, kv_len] matrices: row-major bits,
+    little-endian within each byte, each request from a fresh byte.
+    Returns (uint8 bytes, int64 byte offsets [batch + 1])."""
+    segs = [np.packbits(np.asarray(m, dtype=bool).reshape(-1), bitorder="little")
+            for m in mats]
+    indptr = np.zeros(len(segs) + 1, dtype=np.int64)
+    indptr[1:] = np.cumsum([len(x) for x in segs])
+    data = np.concatenate(segs) if segs else np.zeros(0, np.uint8)
+    return data.astype(np.uint8), indptr
+
+
+def random_tree_parents(rng, n):
+    """Parent of each draft node (-1: a root, hanging off the prefix); nodes are
+    numbered so every parent precedes its children."""
+    return np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, n)], dtype=np.int64)
+
+
+def tree_topology_mask(prefix_len, parents):
+    """[n, prefix_len + n] mask of a draft tree after a shared prefix: node i
+    sees the whole prefix, itself and its ancestors."""
+    n = len(parents)
+    m = np.zeros((n, prefix_len + n), dtype=bool)
+    m[:, :prefix_len] = True
+    for i in range(n):
+        j = i
+        while j >= 0:
+            m[i, prefix_len + j] = True
+            j = int(parents[j])
+    return m
+
+
+def tree_verify(variant=0, batch=16, num_kv_heads=8, tree_size=8, **kw):
+    """Tree-draft verify: per request a random draft tree of tree_size nodes
+    after a prefix ~ U[512, 8192], page 16, Hq 32, D 128, bf16, the topology
+    as a custom mask (causal off)."""
+    rng = np.random.default_rng(1000 * 6 + variant)
+    prefix = rng.integers(512, 8192, size=batch, endpoint=True)
+    parents = [random_tree_parents(rng, tree_size) for _ in range(batch)]
+    w = build(f"tree_verify_b{batch}_hkv{num_kv_heads}", [tree_size] * batch,
+              prefix + tree_size, 32, num_kv_heads, 128, 16, False, -1, BF16, seed=None,
+              rng=rng, **kw)
+    w.custom_mask, w.mask_indptr = pack_custom_mask(
+        [tree_topology_mask(int(p), par) for p, par in zip(prefix, parents)])
+    return w
