@@ -66,6 +66,15 @@ def visible_pairs(w):
     total = 0
     for b in range(w.batch_size):
         Q, L = int(w.qo_lens[b]), int(w.kv_lens[b])
+        if w.custom_mask is not None:   # topology bits, within the left window
+            seg = w.custom_mask[int(w.mask_indptr[b]):int(w.mask_indptr[b + 1])]
+            bits = np.unpackbits(seg, bitorder="little")[:Q * L].reshape(Q, L).astype(bool)
+            if w.window_left >= 0:
+                i = np.arange(Q)[:, None]
+                j = np.arange(L)[None, :]
+                bits &= j + Q + w.window_left >= L + i
+            total += int(bits.sum())
+            continue
         i = np.arange(Q, dtype=np.int64)
         hi = i + L - Q if w.causal else np.full(Q, L - 1)
         hi = np.minimum(hi, L - 1)
@@ -225,6 +234,8 @@ def coverage(pk, torch, dev, iters=20):
     for b in (4, 16, 64):
         for h in (4, 8):
             cases.append((f"verify_b{b}_hkv{h}", W.config4(batch=b, num_kv_heads=h, values=False), {}))
+    for b in (16, 64):
+        cases.append((f"tree_verify_b{b}_hkv8_8nodes", W.tree_verify(batch=b, values=False), {}))
     for ql in (1, 64):
         for wl in (-1, 4095):
             cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",

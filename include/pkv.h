@@ -79,6 +79,19 @@ typedef struct {
      2: short-query tile (16 or 32 packed rows x 128 keys). */
   int32_t tile;
   int32_t reserved[4];
+  /* Topology mask for tree-draft verification (PR #362, Architecture /
+     design notes: a causal mask verifies chain drafts only, tree drafts need
+     a custom mask).  Host arrays, or NULL for none.  Request b's mask is the
+     row-major [qo_len, kv_len] bit matrix (query i, key j) -> bit
+     i * kv_len + j, little-endian within each byte (bit k in byte k / 8 at
+     bit k % 8), starting at byte mask_indptr[b]; mask_indptr has batch + 1
+     non-decreasing entries, each segment holding at least
+     ceil(qo_len * kv_len / 8) bytes, mask_indptr[batch] <= 2^28.  Key j is
+     attended by row i when its bit is set and the left window (if any)
+     allows it; causal must be 0 (the mask replaces it).  The plan copies the
+     bits into its int workspace. */
+  const uint8_t* custom_mask;
+  const int64_t* mask_indptr;
 } pkv_plan_options;
 
 /* Scheduling summary of a plan. */

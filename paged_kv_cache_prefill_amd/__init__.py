@@ -52,7 +52,8 @@ class PkvError(ValueError):
 class _PlanOptions(ctypes.Structure):
     _fields_ = [("num_kv_chunks", ctypes.c_int32), ("kv_begin", ctypes.c_int32),
                 ("kv_end", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("reserved", ctypes.c_int32 * 4),
+                ("custom_mask", ctypes.c_void_p), ("mask_indptr", ctypes.c_void_p)]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -159,10 +160,19 @@ def _ptr_i32(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if a is not None and a.size else None
 
 
-def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0):
+def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0, custom_mask=None,
+             mask_indptr=None):
     o = _PlanOptions()
     o.num_kv_chunks, o.kv_begin, o.kv_end, o.tile = int(num_kv_chunks), int(kv_begin), \
         int(kv_end), int(tile)
+    if custom_mask is not None or mask_indptr is not None:
+        if custom_mask is None or mask_indptr is None:
+            raise PkvError(PKV_EINVAL, "custom_mask and mask_indptr: expected both or neither")
+        m = np.ascontiguousarray(np.asarray(custom_mask).reshape(-1), dtype=np.uint8)
+        ind = np.ascontiguousarray(np.asarray(mask_indptr).reshape(-1), dtype=np.int64)
+        o.custom_mask = m.ctypes.data if m.size else None
+        o.mask_indptr = ind.ctypes.data
+        o._keep = (m, ind)   # the arrays must outlive the call
     return o
 
 
@@ -359,29 +369,33 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
 
 def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, num_kv_heads,
          head_dim, page_size, causal, window_left=-1, sm_scale=None, dtype="bf16",
-         device="cuda", stream=None, num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0):
+         device="cuda", stream=None, num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
+         custom_mask=None, mask_indptr=None):
     """Validate and schedule a batch; returns a runnable Plan.
 
     Host int arrays: qo_indptr[B+1], kv_indptr[B+1], kv_page_indices[kv_indptr[B]],
     kv_last_page_len[B].  sm_scale defaults to 1/sqrt(head_dim).
     num_kv_chunks / kv_begin / kv_end / tile: optional scheduling knobs (see include/pkv.h).
+    custom_mask (packed uint8 bits) / mask_indptr (int64 byte offsets [B+1]): a
+    per-request topology mask for tree drafts, with causal=False (see include/pkv.h).
     """
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
                       device, False, stream,
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
-                           tile=tile))
+                           tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr))
 
 
 def plan_host(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
               num_kv_heads, head_dim, page_size, causal, window_left=-1, sm_scale=None,
-              dtype="bf16", num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0):
+              dtype="bf16", num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
+              custom_mask=None, mask_indptr=None):
     """Validate and schedule without a device: an inspectable, non-runnable Plan."""
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
                       None, True, None,
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
-                           tile=tile))
+                           tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr))
 
 
 def verify_plan(kv_indptr, kv_page_indices, kv_last_page_len, q_len_per_req, num_qo_heads,

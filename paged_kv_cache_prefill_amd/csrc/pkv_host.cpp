@@ -71,9 +71,68 @@ struct Schedule {
   std::vector<MergeItem> merges;
   // int workspace layout
   size_t off_reqs = 0, off_work = 0, off_merge = 0, off_pages = 0, int_bytes = 0;
+  size_t off_mask = 0, mask_bytes = 0;   // custom mask bits (0 bytes: none)
   // float workspace layout
   size_t off_part_lse = 0, float_bytes = 0;
 };
+
+// Bits [bit0, bit0 + n) of a little-endian packed mask are all set?  Returns
+// the index (relative to bit0) of the first clear bit, or n.
+int64_t first_clear_bit(const uint8_t* m, int64_t bit0, int64_t n) {
+  int64_t k = 0;
+  while (k < n && ((bit0 + k) & 7) != 0) {
+    if (!((m[(bit0 + k) >> 3] >> ((bit0 + k) & 7)) & 1)) return k;
+    ++k;
+  }
+  while (k + 64 <= n) {   // whole bytes, eight at a time
+    uint64_t w;
+    std::memcpy(&w, m + ((bit0 + k) >> 3), 8);
+    if (w != ~0ull) break;
+    k += 64;
+  }
+  for (; k < n; ++k)
+    if (!((m[(bit0 + k) >> 3] >> ((bit0 + k) & 7)) & 1)) return k;
+  return n;
+}
+
+// Validate the custom mask of a plan and record, per request, the byte offset
+// of its bits and the length of the key prefix every row keeps (those key
+// tiles need no per-element test).
+pkv_status check_custom_mask(const pkv_plan_options& o, int32_t batch, int32_t causal,
+                             Schedule* S) {
+  if (!o.custom_mask || !o.mask_indptr)
+    return fail(PKV_EINVAL, "custom_mask / mask_indptr: expected both or neither, given %s",
+                o.custom_mask ? "no mask_indptr" : "no custom_mask");
+  if (causal)
+    return fail(PKV_EINVAL, "causal: expected 0 with a custom mask (the mask replaces it), "
+                            "given 1");
+  if (batch > 0 && o.mask_indptr[0] < 0)
+    return fail(PKV_EINVAL, "mask_indptr[0]: expected >= 0, given %lld",
+                (long long)o.mask_indptr[0]);
+  for (int32_t b = 0; b < batch; ++b) {
+    const ReqInfo& r = S->reqs[b];
+    const int64_t need = ((int64_t)r.qo_len * r.kv_len + 7) / 8;
+    const int64_t have = o.mask_indptr[b + 1] - o.mask_indptr[b];
+    if (have < need)
+      return fail(PKV_EINVAL, "mask_indptr: request %d needs >= %lld bytes (qo_len=%d x kv_len=%d "
+                              "bits), given %lld", b, (long long)need, r.qo_len, r.kv_len,
+                  (long long)have);
+  }
+  const int64_t total = batch > 0 ? o.mask_indptr[batch] : 0;
+  if (total > (1ll << 28))
+    return fail(PKV_EINVAL, "mask_indptr[%d]: expected <= 2^28 bytes, given %lld", batch,
+                (long long)total);
+  for (int32_t b = 0; b < batch; ++b) {
+    ReqInfo& r = S->reqs[b];
+    r.mask_off = (int32_t)o.mask_indptr[b];
+    int64_t full = r.kv_len;
+    for (int32_t i = 0; i < r.qo_len && full > 0; ++i)
+      full = first_clear_bit(o.custom_mask, (int64_t)r.mask_off * 8 + (int64_t)i * r.kv_len, full);
+    r.mask_full = (int32_t)full;
+  }
+  S->mask_bytes = (size_t)total;
+  return PKV_OK;
+}
 
 struct RowTask {
   int32_t b, kvh, row0, nrows;
@@ -252,6 +311,10 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     S->max_kv_len = std::max<int32_t>(S->max_kv_len, (int32_t)L);
     max_rows = std::max<int64_t>(max_rows, ql * S->group);
   }
+  if (o.custom_mask || o.mask_indptr) {
+    pkv_status ms = check_custom_mask(o, batch, causal, S);
+    if (ms != PKV_OK) return ms;
+  }
   S->total_q = batch > 0 ? qo_indptr[batch] : 0;
   S->num_indices = batch > 0 ? kv_indptr[batch] : 0;
   S->total_kv = kv_acc;
@@ -415,6 +478,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   off = align_up(off + S->merges.size() * sizeof(MergeItem), 256);
   S->off_pages = off;
   off = align_up(off + (size_t)S->num_indices * sizeof(int32_t), 256);
+  S->off_mask = off;
+  off = align_up(off + S->mask_bytes, 256);
   S->int_bytes = std::max<size_t>(off, 256);
   const size_t part_o = (size_t)slots * MR * head_dim * sizeof(float);
   S->off_part_lse = align_up(part_o, 256);
@@ -558,6 +623,8 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     std::memcpy(blob.data() + S.off_merge, S.merges.data(), S.merges.size() * sizeof(MergeItem));
     if (S.num_indices > 0)
       std::memcpy(blob.data() + S.off_pages, kv_page_indices, S.num_indices * sizeof(int32_t));
+    if (S.mask_bytes > 0)
+      std::memcpy(blob.data() + S.off_mask, opts->custom_mask, S.mask_bytes);
     st = copy_to_device(int_ws, blob, static_cast<hipStream_t>(stream));
     if (st != PKV_OK) {
       delete p;
@@ -711,6 +778,7 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   a.pages = reinterpret_cast<const int32_t*>(p->int_ws + S.off_pages);
   a.reqs = reinterpret_cast<const ReqInfo*>(p->int_ws + S.off_reqs);
   a.work = reinterpret_cast<const WorkItem*>(p->int_ws + S.off_work);
+  a.mask = S.mask_bytes > 0 ? p->int_ws + S.off_mask : nullptr;
   a.part_o = p->float_ws;
   a.part_lse = p->float_ws ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p->float_ws) +
                                                       S.off_part_lse)

@@ -15,7 +15,8 @@ struct ReqInfo {
   int32_t page_off;      // first page-table entry of the request
   int32_t window;        // window_left after normalisation (-1 = no window)
   int32_t kv_out_start;  // first row of the request in a debug gather output
-  int32_t pad0, pad1;
+  int32_t mask_off;      // custom mask: byte offset of the request's bits
+  int32_t mask_full;     // custom mask: keys [0, mask_full) are set for every row
 };
 
 // One work-group task: a tile of packed (position, head-in-group) rows of one
@@ -70,6 +71,7 @@ struct AttnArgs {
   const int32_t* pages;    // device copy of kv_page_indices
   const ReqInfo* reqs;
   const WorkItem* work;
+  const uint8_t* mask;     // custom mask bits (device copy), or nullptr
   float* part_o;           // [slots][tile_rows][head_dim] fp32
   float* part_lse;         // [slots][tile_rows] fp32, log2 domain
   int64_t q_s_tok, q_s_head;

@@ -99,12 +99,15 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // ---- Q fragments (B operand of S^T = K Q^T) and per-row visible ranges
   frag qf[QB][DK];
   int lo[QB], hi[QB];
+  int mrow[QB];   // custom mask: bit index of (row, key 0)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int r = it.row0 + wm * MW + qb * 16 + l16;
     const bool valid = (r - it.row0) < it.nrows && r < R;
+    mrow[qb] = rq.mask_off * 8;
     if (valid) {
       const int pos = r / G;
+      mrow[qb] += pos * rq.kv_len;
       const int h = it.kvh * G + (r - pos * G);
       const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
 #pragma unroll
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     full_lo = max(full_lo, it.key_lo);
     full_hi = a.causal ? pmin + shift_q : rq.kv_len - 1;
     full_hi = min(full_hi, it.kv_end - 1);
+    if (a.mask != nullptr) full_hi = min(full_hi, rq.mask_full - 1);
   }
 
   f32x4 oacc[DB][QB];
@@ -282,7 +286,14 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           float x = s[kb][qb][i];
           if constexpr (MASKED) {
             const int j = jl + kb * 16 + i;
-            x = (j >= lo[qb] && j <= hi[qb]) ? x : kNegInf;
+            bool ok = j >= lo[qb] && j <= hi[qb];
+            if (a.mask != nullptr) {
+              // the key index is clamped into the request so the byte read
+              // stays inside its mask whatever ok is
+              const int bit = mrow[qb] + min(max(j, 0), rq.kv_len - 1);
+              ok = ok && ((a.mask[bit >> 3] >> (bit & 7)) & 1);
+            }
+            x = ok ? x : kNegInf;
             s[kb][qb][i] = x;
           }
           mx = fmaxf(mx, x);

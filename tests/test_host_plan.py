@@ -213,3 +213,28 @@ def test_append_refusals_on_host():
     assert _append_call(lib, ptr=fake, ak_s_tok=260) == pk.PKV_ELAYOUT
     assert _append_call(lib, ptr=fake, k_s_tok=1 << 31) == pk.PKV_ELAYOUT
     assert _append_call(lib, ptr=fake + 8) == pk.PKV_ELAYOUT      # misaligned
+
+
+def test_custom_mask_refusals_and_plan():
+    mats = [W.tree_topology_mask(3, [-1, 0, 0]), W.tree_topology_mask(5, [-1, -1])]
+    data, ind = W.pack_custom_mask(mats)
+    base = dict(qo_indptr=[0, 3, 5], kv_indptr=[0, 2, 4], kv_page_indices=[0, 1, 2, 3],
+                kv_last_page_len=[2, 3], num_qo_heads=8, num_kv_heads=2, head_dim=64,
+                page_size=4, causal=False, window_left=-1)
+    p = pk.plan_host(**base, custom_mask=data, mask_indptr=ind)
+    assert p.info["num_work_items"] > 0
+    ib, _ = pk.workspace_size(**base, custom_mask=data, mask_indptr=ind)
+    ib0, _ = pk.workspace_size(**base)
+    assert ib >= ib0 + len(data)
+    with pytest.raises(pk.PkvError, match="causal"):
+        pk.plan_host(**{**base, "causal": True}, custom_mask=data, mask_indptr=ind)
+    short = ind.copy()
+    short[2] -= 1
+    with pytest.raises(pk.PkvError, match="request 1 needs"):
+        pk.plan_host(**base, custom_mask=data, mask_indptr=short)
+    with pytest.raises(pk.PkvError, match="both or neither"):
+        pk.plan_host(**base, custom_mask=data)
+    bad0 = ind.copy()
+    bad0[0] = -1
+    with pytest.raises(pk.PkvError, match="mask_indptr"):
+        pk.plan_host(**base, custom_mask=data, mask_indptr=bad0)
