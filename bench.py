@@ -262,7 +262,47 @@ def coverage(pk, torch, dev, iters=20):
     for name, w, per_req in (("append_prefill_b8", W.config2(values=False), None),
                              ("append_verify_b64_hkv8", W.config4(batch=64, values=False), 4)):
         rows.append(time_append(pk, torch, dev, name, w, per_req, iters))
+    rows.append(time_sampling(pk, torch, dev, iters))
     return rows
+
+
+def time_sampling(pk, torch, dev, iters):
+    """chain_speculative_sampling over 64 requests x 4 drafts x a 128256-entry
+    vocabulary.  Algorithmic bytes: per draft position examined, its token's
+    two probabilities and its uniform; the row the draw reads (target and draft
+    rows at a rejection, the bonus target row otherwise); the outputs."""
+    inp = W.spec_sampling_inputs()
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in inp.items()}
+    B, n = inp["draft_token_ids"].shape
+    V = inp["target_probs"].shape[2]
+    args = (t["draft_probs"], t["draft_token_ids"], t["target_probs"], t["accept_u"],
+            t["sample_u"])
+    out, acc = pk.chain_speculative_sampling(*args)
+    torch.cuda.synchronize()
+    acc_h = acc.cpu().numpy().astype(np.int64)
+    examined = np.minimum(acc_h + 1, n)
+    nbytes = int((examined * 12).sum() + ((acc_h < n) * 8 * V + (acc_h == n) * 4 * V).sum()
+                 + B * (4 * (n + 1) + 8))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            pk.chain_speculative_sampling(*args, out=out, num_accepted=acc)
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(2, iters // 4))]
+    for a, b in evs:
+        a.record(s)
+        g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 4
+    del g, t
+    torch.cuda.empty_cache()
+    return {"workload": "spec_sampling_b64_n4_v128256", "ms": ms, "GB/s": nbytes / ms / 1e6,
+            "bound": "hbm", "frac": nbytes / ms / 1e6 / PEAK_HBM_GBS,
+            "mean_accepted": float(acc_h.mean())}
 
 
 def time_append(pk, torch, dev, name, w, per_req, iters):

@@ -226,6 +226,37 @@ pkv_status pkv_append_kv(const void* append_k, int64_t ak_s_tok, int64_t ak_s_he
                          pkv_dtype dtype, int32_t* err_count, void* stream);
 
 /*
+ * chain_speculative_sampling: accept or reject each request's chain of draft
+ * tokens against the target model's probabilities, the step after verify
+ * (PR #362, Summary and Architecture / design notes: the acceptance sampler
+ * runs over (batch_size, num_speculate_tokens) and handles chain drafts only).
+ * For request b and draft position t with drafted token x: accept while
+ * accept_u[b][t] * draft_probs[b][t][x] < target_probs[b][t][x] (float32);
+ * at the first rejection emit one token drawn from max(target - draft, 0)
+ * at that position (the target row itself if that is all zero) and stop; if
+ * all are accepted, emit a bonus token drawn from target_probs[b][n].  A draw
+ * takes the smallest index whose running weight sum exceeds
+ * sample_u[b] * (total weight), else the last index with positive weight.
+ * The pages name the step without its formulas; this is standard
+ * speculative (rejection) sampling with the randomness passed in.
+ *   draft_probs [batch][n][vocab], target_probs [batch][n + 1][vocab],
+ *   accept_u [batch][n], sample_u [batch]: packed device float32 arrays;
+ *   draft_token_ids [batch][n]: device int32 (an id outside [0, vocab) is
+ *   rejected, never read).
+ *   output_token_ids [batch][n + 1]: device int32, the accepted drafts, the
+ *   drawn token, then -1; num_accepted [batch]: device int32.
+ * Refused on the host: batch < 0, n < 0, vocab outside [1, 2^20], NULL
+ * pointers when batch > 0, pointers not 4-byte aligned.
+ */
+pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
+                                          const int32_t* draft_token_ids,
+                                          const float* target_probs, const float* accept_u,
+                                          const float* sample_u, int32_t batch,
+                                          int32_t num_speculate_tokens, int32_t vocab_size,
+                                          int32_t* output_token_ids, int32_t* num_accepted,
+                                          void* stream);
+
+/*
  * debug_gather: write the logical K and V rows of every planned request,
  * [sum kv_len, kv_heads, head_dim] in request order, through the same page
  * address path the attention kernel reads (for bit-exact gather checks).

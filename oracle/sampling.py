@@ -21,10 +21,14 @@ spell it out; the reading taken is standard speculative (rejection) sampling:
 
 Draws use inverse-CDF sampling with one extra uniform s per request: the
 smallest k whose running sum of the weights exceeds s * (sum of all
-weights); if rounding leaves none, the last k with a positive weight.
-Randomness is an input (u [B, n], s [B]), so the result is a function.
-Decisions that floating point settles (the accept test, the threshold) are
-taken in float32, the precision of the probabilities the kernel reads.
+weights); if none does, the last k with a positive weight.  Randomness is an
+input (u [B, n], s [B]), so the result is a function.  The accept test is a
+single float32 product and compare, taken exactly as the kernel takes it.
+The draw is taken on the float32 weights with float64 running sums (exact
+for any vocabulary here); a float32 implementation, whose sums round at
+each step, can land on a neighbouring index when s * total falls within its
+summation error of a boundary -- the tests accept such a draw only when it
+is valid within that error bound.
 """
 from __future__ import annotations
 
@@ -34,8 +38,8 @@ import numpy as np
 def inverse_cdf(weights, s):
     """Index drawn from non-negative float32 weights by the uniform s."""
     w = np.asarray(weights, dtype=np.float32)
-    c = np.cumsum(w, dtype=np.float32)
-    thr = np.float32(s) * c[-1]
+    c = np.cumsum(w, dtype=np.float64)
+    thr = float(np.float32(s)) * c[-1]
     hit = np.nonzero(c > thr)[0]
     if hit.size:
         return int(hit[0])

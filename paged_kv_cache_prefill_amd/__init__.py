@@ -26,7 +26,7 @@ import os
 import numpy as np
 
 __all__ = ["plan", "plan_host", "verify_plan", "workspace_size", "merge_states", "append_kv",
-           "Plan",
+           "chain_speculative_sampling", "Plan",
            "PkvError", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -102,12 +102,15 @@ def load_library():
                                   vp, i64, i32, i64, i64, i64,
                                   vp, i64, i32, i64, i64, i64,
                                   ctypes.c_int, vp, vp]
+    lib.pkv_chain_speculative_sampling.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp,
+                                                   vp]
     lib.pkv_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.pkv_plan_get_work.argtypes = [vp, pi32, i64, ctypes.POINTER(i64)]
     lib.pkv_plan_destroy.argtypes = [vp]
     lib.pkv_plan_destroy.restype = None
     for name in ("pkv_workspace_size", "pkv_plan", "pkv_run", "pkv_merge_states",
-                 "pkv_debug_gather", "pkv_append_kv", "pkv_plan_get_info",
+                 "pkv_debug_gather", "pkv_append_kv", "pkv_chain_speculative_sampling",
+                 "pkv_plan_get_info",
                  "pkv_plan_get_work"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -495,3 +498,40 @@ def append_kv(append_k, append_v, batch_indices, positions, kv_indptr, kv_page_i
         _dtype_code(paged_k.dtype), err_count.data_ptr() if err_count is not None else None,
         ctypes.c_void_p(stream.cuda_stream)))
     return paged_k, paged_v
+
+
+def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accept_u, sample_u,
+                               out=None, num_accepted=None, stream=None):
+    """Accept/reject each request's draft chain -> (output_token_ids [B, n+1] int32,
+    num_accepted [B] int32).
+
+    draft_probs [B, n, V] and target_probs [B, n+1, V] float32, draft_token_ids
+    [B, n] int32, accept_u [B, n] and sample_u [B] float32 (uniforms in [0, 1)),
+    all packed on one device.  See include/pkv.h for the rule."""
+    torch = _torch()
+    lib = load_library()
+    if target_probs.dim() != 3:
+        raise PkvError(PKV_EINVAL, "target_probs: expected [batch, n + 1, vocab]")
+    B, n1, V = target_probs.shape
+    n = n1 - 1
+    dev = target_probs.device
+    want = (("draft_probs", draft_probs, torch.float32, (B, n, V)),
+            ("draft_token_ids", draft_token_ids, torch.int32, (B, n)),
+            ("target_probs", target_probs, torch.float32, (B, n + 1, V)),
+            ("accept_u", accept_u, torch.float32, (B, n)),
+            ("sample_u", sample_u, torch.float32, (B,)))
+    for name, t, dt, shape in want:
+        if t.dtype != dt or tuple(t.shape) != shape or t.device != dev or not t.is_contiguous():
+            raise PkvError(PKV_EMISMATCH, f"{name}: expected a packed {dt} tensor {shape} on "
+                                          f"{dev}, given {t.dtype} {tuple(t.shape)}")
+    if out is None:
+        out = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(lib.pkv_chain_speculative_sampling(
+        draft_probs.data_ptr(), draft_token_ids.data_ptr(), target_probs.data_ptr(),
+        accept_u.data_ptr(), sample_u.data_ptr(), B, n, V, out.data_ptr(),
+        num_accepted.data_ptr(), ctypes.c_void_p(stream.cuda_stream)))
+    return out, num_accepted

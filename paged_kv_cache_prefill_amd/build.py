@@ -47,15 +47,17 @@ def build(verbose=False):
     tmp = tempfile.mkdtemp(prefix="pkv_build_")
     try:
         kobj = os.path.join(tmp, "pkv_kernels.o")
+        sobj = os.path.join(tmp, "pkv_sampling.o")
         hobj = os.path.join(tmp, "pkv_host.o")
         steps = [
             [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "pkv_kernels.hip"), "-o", kobj],
+            [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "pkv_sampling.hip"), "-o", sobj],
             [gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "pkv_host.cpp"), "-o", hobj],
         ]
-        with ThreadPoolExecutor(max_workers=2) as ex:
+        with ThreadPoolExecutor(max_workers=3) as ex:
             outs = list(ex.map(_run, steps))
         out_tmp = os.path.join(tmp, "libpkv.so")
-        outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj,
+        outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, sobj, hobj,
                           "-o", out_tmp, f"-L{ROCM}/lib", "-lamdhip64"]))
         staged = LIB + ".tmp"
         shutil.copyfile(out_tmp, staged)

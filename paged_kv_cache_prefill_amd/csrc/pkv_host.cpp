@@ -914,6 +914,46 @@ pkv_status pkv_append_kv(const void* append_k, int64_t ak_s_tok, int64_t ak_s_he
   return PKV_OK;
 }
 
+pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
+                                          const int32_t* draft_token_ids,
+                                          const float* target_probs, const float* accept_u,
+                                          const float* sample_u, int32_t batch,
+                                          int32_t num_speculate_tokens, int32_t vocab_size,
+                                          int32_t* output_token_ids, int32_t* num_accepted,
+                                          void* stream) {
+  g_err.clear();
+  if (batch < 0) return fail(PKV_EINVAL, "batch_size: expected >= 0, given %d", batch);
+  if (num_speculate_tokens < 0)
+    return fail(PKV_EINVAL, "num_speculate_tokens: expected >= 0, given %d", num_speculate_tokens);
+  if (vocab_size < 1 || vocab_size > (1 << 20))
+    return fail(PKV_EINVAL, "vocab_size: expected in [1, 2^20], given %d", vocab_size);
+  if (batch == 0) return PKV_OK;
+  const bool need_draft = num_speculate_tokens > 0;
+  if (!target_probs || !sample_u || !output_token_ids || !num_accepted ||
+      (need_draft && (!draft_probs || !draft_token_ids || !accept_u)))
+    return fail(PKV_EINVAL, "chain_speculative_sampling: expected device pointers, given NULL");
+  for (const void* ptr : {(const void*)draft_probs, (const void*)draft_token_ids,
+                          (const void*)target_probs, (const void*)accept_u,
+                          (const void*)sample_u, (const void*)output_token_ids,
+                          (const void*)num_accepted})
+    if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0)
+      return fail(PKV_ELAYOUT, "chain_speculative_sampling: expected 4-byte aligned pointers");
+  SampleArgs a;
+  a.draft_probs = draft_probs;
+  a.draft_ids = draft_token_ids;
+  a.target_probs = target_probs;
+  a.accept_u = accept_u;
+  a.sample_u = sample_u;
+  a.out_ids = output_token_ids;
+  a.num_accepted = num_accepted;
+  a.batch = batch;
+  a.num_spec = num_speculate_tokens;
+  a.vocab = vocab_size;
+  hipError_t e = launch_spec_sample(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "speculative sampling launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_t k_page_size,
                             int32_t k_heads, int32_t k_dim, int64_t k_s_page, int64_t k_s_tok,
                             int64_t k_s_head, const void* v, int64_t v_pages,

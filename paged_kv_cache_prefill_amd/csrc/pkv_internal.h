@@ -138,6 +138,17 @@ struct AppendArgs {
   uint32_t page_magic, page_shift;
 };
 
+struct SampleArgs {
+  const float* draft_probs;    // [batch][num_spec][vocab]
+  const int32_t* draft_ids;    // [batch][num_spec]
+  const float* target_probs;   // [batch][num_spec + 1][vocab]
+  const float* accept_u;       // [batch][num_spec]
+  const float* sample_u;       // [batch]
+  int32_t* out_ids;            // [batch][num_spec + 1]
+  int32_t* num_accepted;       // [batch]
+  int32_t batch, num_spec, vocab;
+};
+
 // dtype: 0 fp16, 1 bf16, 2 fp32 (merge_states only).
 hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
                             hipStream_t stream);
@@ -150,5 +161,6 @@ hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,
 hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a,
                                hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_spec_sample(const SampleArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -29,14 +29,14 @@ def test_inverse_cdf_matches_a_loop():
         if w.sum() == 0:
             w[int(rng.integers(V))] = 1.0
         s = float(rng.random())
-        total = np.float32(0)
+        total = 0.0
         for x in w:
-            total = np.float32(total + x)
-        thr = np.float32(s) * total
-        run = np.float32(0)
+            total += float(x)
+        thr = float(np.float32(s)) * total
+        run = 0.0
         want = None
         for k, x in enumerate(w):
-            run = np.float32(run + x)
+            run += float(x)
             if run > thr:
                 want = k
                 break

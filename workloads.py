@@ -271,3 +271,35 @@ def tree_verify(variant=0, batch=16, num_kv_heads=8, tree_size=8, **kw):
     w.custom_mask, w.mask_indptr = pack_custom_mask(
         [tree_topology_mask(int(p), par) for p, par in zip(prefix, parents)])
     return w
+
+
+
+# ----------------------------------------------------------------------------
+# Chain speculative sampling: draft / target distributions and uniforms
+# ----------------------------------------------------------------------------
+
+def _softmax32(logits):
+    z = logits - logits.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def spec_sampling_inputs(variant=0, batch=64, num_spec=4, vocab=128256, spread=3.0,
+                         draft_noise=1.0):
+    """Target probabilities softmax(N(0, spread^2) logits) over the vocabulary at
+    num_spec + 1 positions; draft probabilities from the same logits plus
+    N(0, draft_noise^2) noise at the first num_spec (a correlated draft model);
+    draft tokens drawn from the draft probabilities; accept / sample uniforms
+    in [0, 1).  float32 throughout, draft ids int32."""
+    rng = np.random.default_rng(1000 * 7 + variant)
+    logits = rng.standard_normal((batch, num_spec + 1, vocab), dtype=np.float32) * spread
+    target = _softmax32(logits)
+    noisy = logits[:, :num_spec] + rng.standard_normal((batch, num_spec, vocab),
+                                                       dtype=np.float32) * draft_noise
+    draft = _softmax32(noisy)
+    cdf = np.cumsum(draft.astype(np.float64), axis=-1)
+    u = rng.random((batch, num_spec))
+    ids = np.minimum((cdf < (u * cdf[..., -1])[..., None]).sum(axis=-1), vocab - 1)
+    return dict(draft_probs=draft, draft_token_ids=ids.astype(np.int32), target_probs=target,
+                accept_u=rng.random((batch, num_spec), dtype=np.float32),
+                sample_u=rng.random(batch, dtype=np.float32))
