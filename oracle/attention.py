@@ -16,6 +16,7 @@ matmul / exp / log as the only library steps:
 * ``merge_states`` / ``merge_many`` -- combining partial (o, lse) states.
 * ``append_paged_kv``   -- writing new K/V rows into their pages.
 * ``custom_mask_rows``  -- a request's topology mask (tree drafts) from packed bits.
+* ``soft_cap``          -- the logits soft-cap transform.
 
 Sources (web pages of the AMD-Ecosystem FlashInfer fork):
   [W]  PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
@@ -33,6 +34,9 @@ Sources (web pages of the AMD-Ecosystem FlashInfer fork):
        split-KV test commit (partial (o, lse) states merged into one result).
   [T]  PR #362, Architecture / design notes: a causal mask verifies chain
        drafts only; tree drafts need a topology mask (custom_mask).
+  [S]  PR #362, Architecture / design notes and per-commit messages: a
+       logits soft-cap exists and a route that ignores it gives a wrong
+       answer (the pages gate on it but do not give the formula).
 
 Readings where the pages are silent (each also listed in the design notes):
   * kv_len = (n_pages - 1) * page_size + last_page_len, 0 for no pages.
@@ -48,6 +52,8 @@ Readings where the pages are silent (each also listed in the design notes):
     little-endian (bit k sits in byte k // 8 at bit k % 8) from byte
     mask_indptr[b].  It replaces the causal mask (causal must be off); the
     left window still applies on top of it.
+  * logits soft-cap [S]: with cap > 0 every scaled logit s becomes
+    cap * tanh(s / cap) before the softmax (cap = 0: no cap).
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (brute force, closed forms, library routines, invariants, golden fixtures).
 """
@@ -112,6 +118,15 @@ def allowed_mask(qo_len, kv_len, causal, window_left, kv_begin=None, kv_end=None
     return ok
 
 
+def soft_cap(s, cap):
+    """cap * tanh(s / cap) for cap > 0, s unchanged for cap = 0 [S]."""
+    if cap is None or cap == 0:
+        return s
+    if not cap > 0:
+        raise ValueError(f"logits_soft_cap: expected >= 0, given {cap}")
+    return cap * np.tanh(np.asarray(s, dtype=np.float64) / cap)
+
+
 def custom_mask_rows(custom_mask, mask_indptr, b, qo_len, kv_len):
     """Boolean [qo_len, kv_len] topology mask of request b from packed bits [T].
 
@@ -147,7 +162,7 @@ def _check_heads(num_qo_heads, num_kv_heads):
 def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
               kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
               window_left, sm_scale, kv_begin=None, kv_end=None, custom_mask=None,
-              mask_indptr=None):
+              mask_indptr=None, logits_soft_cap=0.0):
     """Masked softmax attention over a paged KV cache, in float64.
 
     q: [total_q, Hq, D]; k_pool, v_pool: NHD [num_pages, P, Hkv, D].
@@ -160,7 +175,7 @@ def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
     kv_begin/kv_end (optional) restrict every request to keys in that range of
     its own key coordinates, giving the partial state of one KV chunk.
     custom_mask/mask_indptr (optional, packed bits [T]) intersect the mask with
-    each request's topology mask.
+    each request's topology mask; logits_soft_cap > 0 caps every s_ij [S].
     """
     _check_heads(num_qo_heads, num_kv_heads)
     use_custom = _check_custom(custom_mask, mask_indptr, causal)
@@ -184,7 +199,7 @@ def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
         has_key = mask.any(axis=1)
         for h in range(hq):
             g = h // group
-            s = sm_scale * (q[q0:q1, h, :] @ kb[:, g, :].T)
+            s = soft_cap(sm_scale * (q[q0:q1, h, :] @ kb[:, g, :].T), logits_soft_cap)
             s = np.where(mask, s, NEG_INF)
             m = np.max(s, axis=1, initial=NEG_INF)
             m_safe = np.where(has_key, m, 0.0)
@@ -200,7 +215,7 @@ def attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
 def attention_bruteforce(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
                          kv_last_page_len, num_qo_heads, num_kv_heads, page_size,
                          causal, window_left, sm_scale, kv_begin=None, kv_end=None,
-                         custom_mask=None, mask_indptr=None):
+                         custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
     """The same definition as ``attention`` as literal per-element loops.
 
     Pure Python floats (IEEE double), no NumPy arithmetic: for tiny inputs only.
@@ -245,7 +260,10 @@ def attention_bruteforce(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indice
                     dot = 0.0
                     for t in range(d):
                         dot += float(q[row][h][t]) * float(k_pool[page][slot][g][t])
-                    scores.append(sm_scale * dot)
+                    sc = sm_scale * dot
+                    if logits_soft_cap:
+                        sc = logits_soft_cap * math.tanh(sc / logits_soft_cap)
+                    scores.append(sc)
                     values.append([float(v_pool[page][slot][g][t]) for t in range(d)])
                 if not scores:
                     continue
@@ -300,7 +318,7 @@ def merge_many(os, lses):
 def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
                    kv_last_page_len, num_qo_heads, num_kv_heads, page_size, causal,
                    window_left, sm_scale, b, rows, heads, kv_begin=None, kv_end=None,
-                   custom_mask=None, mask_indptr=None):
+                   custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
     """``attention`` restricted to some rows and q heads of request b.
 
     Same definition, float64; used to check full-size workloads on sampled
@@ -330,7 +348,8 @@ def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
             ok = mask[i]
             if not ok.any():
                 continue
-            s = sm_scale * (kb[ok] @ np.asarray(q[q0 + i, h, :], dtype=np.float64))
+            s = soft_cap(sm_scale * (kb[ok] @ np.asarray(q[q0 + i, h, :], dtype=np.float64)),
+                         logits_soft_cap)
             m = s.max()
             e = np.exp(s - m)
             total = e.sum()

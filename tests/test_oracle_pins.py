@@ -632,3 +632,44 @@ def test_custom_mask_rows_match_full():
         q0 = int(w.qo_indptr[b])
         assert np.allclose(o_r, o[q0:q0 + len(rows)][:, heads], atol=1e-12)
         assert np.allclose(l_r, lse[q0:q0 + len(rows)][:, heads], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# logits soft-cap
+# ---------------------------------------------------------------------------
+def test_soft_cap_golden():
+    with open(os.path.join(GOLDEN, "soft_cap.json")) as f:
+        g = json.load(f)
+    q = np.ones((1, 1, 1))
+    k = np.array(g["raw_dot"], dtype=np.float64).reshape(1, 2, 1, 1)
+    v = np.array(g["v"], dtype=np.float64).reshape(1, 2, 1, 1)
+    o, lse = oracle.attention(q, k, v, [0, 1], [0, 1], [0], [2], 1, 1, 2, False, -1,
+                              g["sm_scale"], logits_soft_cap=g["cap"])
+    assert abs(lse[0, 0] - g["lse"]) < 1e-12 and abs(o[0, 0, 0] - g["o"]) < 1e-12
+    ob, lb = oracle.attention_bruteforce(q, k, v, [0, 1], [0, 1], [0], [2], 1, 1, 2, False, -1,
+                                         g["sm_scale"], logits_soft_cap=g["cap"])
+    assert abs(lb[0, 0] - g["lse"]) < 1e-12 and abs(ob[0, 0, 0] - g["o"]) < 1e-12
+
+
+def test_soft_cap_bounds_limit_and_bruteforce():
+    w = W.build("cap", [6, 3], [20, 9], 4, 2, 8, 4, True, 5, W.FP16, seed=91)
+    q, k, v = w.float_inputs()
+    a = w.plan_args()
+    del a["head_dim"]
+    base = oracle.attention(q, k, v, **a)
+    # a cap far above every logit changes nothing measurable
+    far = oracle.attention(q, k, v, **a, logits_soft_cap=1e9)
+    assert np.allclose(far[0], base[0], atol=1e-12) and np.allclose(far[1], base[1], atol=1e-12)
+    # brute force agrees at a biting cap
+    big = {**a, "sm_scale": 40.0}
+    o1, l1 = oracle.attention(q, k, v, **big, logits_soft_cap=2.0)
+    o2, l2 = oracle.attention_bruteforce(q, k, v, **big, logits_soft_cap=2.0)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    # every capped logit lies in (-cap, cap): lse within log(#visible) +- cap
+    counts = np.concatenate([oracle.allowed_mask(int(ql), int(kl), True, 5).sum(1)
+                             for ql, kl in zip(w.qo_lens, w.kv_lens)])
+    assert (l1 <= 2.0 + np.log(counts)[:, None] + 1e-12).all()
+    assert (l1 >= -2.0 + np.log(counts)[:, None] - 1e-12).all()
+    # and the cap bites: the uncapped scores at that scale differ
+    o3, _ = oracle.attention(q, k, v, **big)
+    assert np.abs(o3 - o1).max() > 0.1
