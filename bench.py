@@ -236,6 +236,9 @@ def coverage(pk, torch, dev, iters=20):
             cases.append((f"verify_b{b}_hkv{h}", W.config4(batch=b, num_kv_heads=h, values=False), {}))
     for b in (16, 64):
         cases.append((f"tree_verify_b{b}_hkv8_8nodes", W.tree_verify(batch=b, values=False), {}))
+    capped = W.config2(values=False)
+    capped.logits_soft_cap = 50.0
+    cases.append(("paged_prefill_b8_softcap50", capped, {}))
     for ql in (1, 64):
         for wl in (-1, 4095):
             cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",

@@ -92,6 +92,11 @@ typedef struct {
      bits into its int workspace. */
   const uint8_t* custom_mask;
   const int64_t* mask_indptr;
+  /* Logits soft-cap (PR #362, Architecture / design notes and per-commit
+     messages gate on it; the formula is the reading taken): with cap > 0
+     every scaled logit s = sm_scale * q.k becomes cap * tanh(s / cap) before
+     the softmax, and lse is taken over the capped logits.  0: no cap. */
+  float logits_soft_cap;
 } pkv_plan_options;
 
 /* Scheduling summary of a plan. */

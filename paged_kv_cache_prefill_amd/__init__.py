@@ -53,7 +53,8 @@ class _PlanOptions(ctypes.Structure):
     _fields_ = [("num_kv_chunks", ctypes.c_int32), ("kv_begin", ctypes.c_int32),
                 ("kv_end", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("reserved", ctypes.c_int32 * 4),
-                ("custom_mask", ctypes.c_void_p), ("mask_indptr", ctypes.c_void_p)]
+                ("custom_mask", ctypes.c_void_p), ("mask_indptr", ctypes.c_void_p),
+                ("logits_soft_cap", ctypes.c_float)]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -164,10 +165,11 @@ def _ptr_i32(a):
 
 
 def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0, custom_mask=None,
-             mask_indptr=None):
+             mask_indptr=None, logits_soft_cap=0.0):
     o = _PlanOptions()
     o.num_kv_chunks, o.kv_begin, o.kv_end, o.tile = int(num_kv_chunks), int(kv_begin), \
         int(kv_end), int(tile)
+    o.logits_soft_cap = float(logits_soft_cap or 0.0)
     if custom_mask is not None or mask_indptr is not None:
         if custom_mask is None or mask_indptr is None:
             raise PkvError(PKV_EINVAL, "custom_mask and mask_indptr: expected both or neither")
@@ -373,7 +375,7 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
 def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, num_kv_heads,
          head_dim, page_size, causal, window_left=-1, sm_scale=None, dtype="bf16",
          device="cuda", stream=None, num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
-         custom_mask=None, mask_indptr=None):
+         custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
     """Validate and schedule a batch; returns a runnable Plan.
 
     Host int arrays: qo_indptr[B+1], kv_indptr[B+1], kv_page_indices[kv_indptr[B]],
@@ -381,24 +383,27 @@ def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, 
     num_kv_chunks / kv_begin / kv_end / tile: optional scheduling knobs (see include/pkv.h).
     custom_mask (packed uint8 bits) / mask_indptr (int64 byte offsets [B+1]): a
     per-request topology mask for tree drafts, with causal=False (see include/pkv.h).
+    logits_soft_cap > 0 caps every scaled logit s to cap * tanh(s / cap).
     """
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
                       device, False, stream,
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
-                           tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr))
+                           tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr,
+                           logits_soft_cap=logits_soft_cap))
 
 
 def plan_host(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
               num_kv_heads, head_dim, page_size, causal, window_left=-1, sm_scale=None,
               dtype="bf16", num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
-              custom_mask=None, mask_indptr=None):
+              custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
     """Validate and schedule without a device: an inspectable, non-runnable Plan."""
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
                       None, True, None,
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
-                           tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr))
+                           tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr,
+                           logits_soft_cap=logits_soft_cap))
 
 
 def verify_plan(kv_indptr, kv_page_indices, kv_last_page_len, q_len_per_req, num_qo_heads,

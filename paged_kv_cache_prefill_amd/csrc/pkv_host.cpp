@@ -251,6 +251,9 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     return fail(PKV_EINVAL, "opts.kv_end: expected >= kv_begin=%d or < 0, given %d", o.kv_begin,
                 o.kv_end);
   if (o.tile < 0 || o.tile > 2) return fail(PKV_EINVAL, "opts.tile: expected 0, 1 or 2, given %d", o.tile);
+  if (!(o.logits_soft_cap >= 0.f) || !std::isfinite(o.logits_soft_cap))
+    return fail(PKV_EINVAL, "opts.logits_soft_cap: expected a finite value >= 0, given %g",
+                (double)o.logits_soft_cap);
   const int64_t opt_end = o.kv_end < 0 ? INT64_MAX : o.kv_end;
 
   const int32_t qi0 = batch > 0 ? qo_indptr[0] : 0;
@@ -542,6 +545,7 @@ struct pkv_plan_s {
   Schedule S;
   pkv_dtype dtype;
   float sm_scale;
+  float soft_cap = 0.f;
   uint32_t page_magic = 1, page_shift = 0;
   uint8_t* int_ws = nullptr;
   float* float_ws = nullptr;
@@ -596,6 +600,7 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
   const Schedule& S = p->S;
   p->dtype = dtype;
   p->sm_scale = sm_scale;
+  p->soft_cap = opts ? opts->logits_soft_cap : 0.f;
   page_divider((uint32_t)page_size, &p->page_magic, &p->page_shift);
   const bool dry = (int_ws == nullptr && int_ws_bytes == 0);
   if (!dry) {
@@ -799,6 +804,8 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   a.page_shift = p->page_shift;
   a.causal = S.causal;
   a.scale_log2 = p->sm_scale * 1.4426950408889634f;
+  a.cap_in = p->soft_cap > 0.f ? p->sm_scale / p->soft_cap : 0.f;
+  a.cap_out = p->soft_cap > 0.f ? p->soft_cap * 1.4426950408889634f : 0.f;
   hipError_t e = launch_attention(S.tile_kind, (int)p->dtype, S.head_dim, a, hs);
   if (e != hipSuccess) return fail(PKV_EHIP, "attention launch: %s", hipGetErrorString(e));
   if (!S.merges.empty()) {

@@ -88,6 +88,10 @@ struct AttnArgs {
   uint32_t page_shift;
   int32_t causal;
   float scale_log2;        // sm_scale * log2(e)
+  // logits soft-cap, log2 domain: s' = cap_out * tanh(raw * cap_in)
+  // = cap * log2(e) * tanh(sm_scale * raw / cap); cap_out = 0: no cap
+  float cap_in;            // sm_scale / cap
+  float cap_out;           // cap * log2(e)
 };
 
 struct SplitMergeArgs {

@@ -267,6 +267,33 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 
     // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
     const int jl = j0 + wn * NW + 4 * g;
+    // logits soft-cap: scores become cap * log2(e) * tanh(sm_scale * s / cap),
+    // already in log2 units; masked scores are set to -inf after this, below.
+    // tanh(y) is 1 - 2 / (1 + e^{2y}) (exp2 and a reciprocal) for |y| >= 1/4
+    // and its Taylor series y (1 - y^2/3 + 2y^4/15 - 17y^6/315) below, where
+    // the first form would lose the small value to cancellation (relative
+    // error of either below 1e-6, so a large cap reproduces the plain logit).
+    const bool capped = a.cap_out != 0.f;
+    const float mul = capped ? 1.f : a.scale_log2;
+    if (capped) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = s[kb][qb][i] * a.cap_in;
+            const float y2 = y * y;
+            const float series =
+                y * __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2, -17.f / 315.f,
+                                                                         2.f / 15.f),
+                                                      -1.f / 3.f),
+                                   1.f);
+            const float e = fast_exp2(y * 2.8853900817779268f);   // e^{2y}
+            const float big = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
+            s[kb][qb][i] = (fabsf(y) < 0.25f ? series : big) * a.cap_out;
+          }
+    }
     // Lazy rescaling: exponents are taken against a reference m_run per row
     // that moves only when a score exceeds it by more than kTau (log2 units),
     // so every p stays <= 2^kTau; the reference cancels in o = sum p v / sum p
@@ -299,7 +326,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           mx = fmaxf(mx, x);
         }
       }
-      mloc[qb] = mx * a.scale_log2;
+      mloc[qb] = mx * mul;
       grow = grow || (mloc[qb] > m_run[qb] + kTau);
     }
     if (wave_any(grow)) {
@@ -323,7 +350,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][qb][i], a.scale_log2, -m_use));
+          const float p = fast_exp2(__builtin_fmaf(s[kb][qb][i], mul, -m_use));
           s[kb][qb][i] = p;
           rs += p;
         }

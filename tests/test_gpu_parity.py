@@ -401,3 +401,41 @@ def test_run_refuses_mismatches(pk):
     qkv[:, :8] = q
     o_s, _ = p.run(qkv[:, :8], k, v)
     assert torch.equal(o_s, o_ref)
+
+
+# ---------------------------------------------------------------------------
+# logits soft-cap
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cap", [2.0, 30.0])
+@pytest.mark.parametrize("d,dtype", [(64, W.FP16), (128, W.BF16)])
+def test_soft_cap_tiny(pk, cap, d, dtype):
+    rng = np.random.default_rng(int(cap) * 7 + d)
+    qo = [1, 17, 40]
+    kv = [30, 17, 200]
+    for causal, wl in ((True, -1), (False, 9), (True, 50)):
+        # a large sm_scale makes the cap bite on N(0, 1) data
+        w = W.build("cap", qo, kv, 8, 2, d, 16, causal, wl, dtype,
+                    seed=int(rng.integers(1 << 30)), poison=True, sm_scale=0.5)
+        w.logits_soft_cap = cap
+        ref_o, ref_lse = oracle_full(w)
+        tensors = device_inputs(w)
+        for tile in (1, 2):
+            o, lse, _ = run(pk, w, tensors, tile=tile)
+            assert_close(o, lse, ref_o, ref_lse, dtype,
+                         f"cap={cap} d={d} causal={causal} w={wl} tile={tile}")
+
+
+def test_soft_cap_full_size(pk):
+    w = W.config2(poison=True)
+    w.logits_soft_cap = 5.0
+    w.sm_scale = 0.3
+    floats = w.float_inputs()
+    o, lse, _ = run(pk, w)
+    check_sampled(w, o, lse, np.random.default_rng(12), "config2 cap 5", floats=floats,
+                  per_request=2, heads=3)
+    # a cap far above every logit gives the uncapped result
+    w2 = W.config4(batch=16, num_kv_heads=8, poison=True)
+    o_a, l_a, _ = run(pk, w2)
+    w2.logits_soft_cap = 1e6
+    o_b, l_b, _ = run(pk, w2)
+    assert np.abs(o_a - o_b).max() <= 1e-2 and np.abs(l_a - l_b).max() <= 1e-3

@@ -85,6 +85,7 @@ class Workload:
     v_pool: np.ndarray = None
     custom_mask: np.ndarray = None   # packed topology bits (uint8) and their
     mask_indptr: np.ndarray = None   # per-request byte offsets, or None
+    logits_soft_cap: float = 0.0     # 0: no cap
 
     @property
     def batch_size(self):
@@ -103,7 +104,9 @@ class Workload:
                     causal=self.causal, window_left=self.window_left,
                     sm_scale=self.sm_scale,
                     **({} if self.custom_mask is None else
-                       dict(custom_mask=self.custom_mask, mask_indptr=self.mask_indptr)))
+                       dict(custom_mask=self.custom_mask, mask_indptr=self.mask_indptr)),
+                    **({} if not self.logits_soft_cap else
+                       dict(logits_soft_cap=self.logits_soft_cap)))
 
     def float_inputs(self):
         return (to_float(self.q, self.dtype), to_float(self.k_pool, self.dtype),
