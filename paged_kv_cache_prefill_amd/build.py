@@ -46,18 +46,16 @@ def build(verbose=False):
     gxx = shutil.which("g++") or "g++"
     tmp = tempfile.mkdtemp(prefix="pkv_build_")
     try:
-        kobj = os.path.join(tmp, "pkv_kernels.o")
-        sobj = os.path.join(tmp, "pkv_sampling.o")
+        hip_srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+        objs = [os.path.join(tmp, f[:-4] + ".o") for f in hip_srcs]
         hobj = os.path.join(tmp, "pkv_host.o")
-        steps = [
-            [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "pkv_kernels.hip"), "-o", kobj],
-            [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "pkv_sampling.hip"), "-o", sobj],
-            [gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "pkv_host.cpp"), "-o", hobj],
-        ]
-        with ThreadPoolExecutor(max_workers=3) as ex:
+        steps = [[hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, f), "-o", o]
+                 for f, o in zip(hip_srcs, objs)]
+        steps.append([gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "pkv_host.cpp"), "-o", hobj])
+        with ThreadPoolExecutor(max_workers=min(8, len(steps))) as ex:
             outs = list(ex.map(_run, steps))
         out_tmp = os.path.join(tmp, "libpkv.so")
-        outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, sobj, hobj,
+        outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, hobj,
                           "-o", out_tmp, f"-L{ROCM}/lib", "-lamdhip64"]))
         staged = LIB + ".tmp"
         shutil.copyfile(out_tmp, staged)

@@ -1,0 +1,558 @@
+// The attention kernel template and its launchers, shared by the HIP files
+// that instantiate its variants (plain, custom mask, soft-cap, both).  What
+// it computes and how is described in pkv_kernels.hip.  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+// WM waves split the rows, WN waves split the keys of each LDS tile;
+// each wave owns QB blocks of 16 rows and NW keys of the tile.  WPE is the
+// number of waves per SIMD the register budget is sized for.  PM selects the
+// page addressing: 0 any page size (per-key page-table lookup), 1 power-of-
+// two pages shorter than one load instruction's rows (each lane's slot is
+// fixed on complete tiles), 3 power-of-two pages of at least one load
+// instruction's rows: each instruction stays on one page, so its page id is
+// a scalar load and its address an SGPR base plus a per-lane 32-bit offset,
+// issued from assembly (dma16), which the compiler does not track; the
+// wait-all and barrier closing every tile make those loads visible.  With PM
+// 0 and 1 the last, partial tile of a task takes the general path.  VAR bit
+// 0 adds the custom-mask test on edge tiles, bit 1 the logits soft-cap; each
+// combination is its own instantiation so the plain kernel carries neither.
+template <typename T, int D, int WM, int WN, int QB, int NW, int WPE, int PM, int VAR>
+__global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
+  constexpr bool kMask = (VAR & 1) != 0;   // custom topology mask
+  constexpr bool kCap = (VAR & 2) != 0;    // logits soft-cap
+  using Tr = Traits<T>;
+  using frag = typename Tr::frag;
+  constexpr int NWAVE = WM * WN;
+  constexpr int MW = 16 * QB;           // rows per wave
+  constexpr int NWG = NW * WN;          // keys per LDS tile
+  constexpr int CH = D / 8;             // 16-byte chunks per key row
+  constexpr int TCH = NWG * CH;         // chunks per tile (K or V)
+  constexpr int NI = TCH / (64 * NWAVE);  // direct-load instructions per wave per tile
+  constexpr int RPI = 64 / CH;          // key rows filled by one wave instruction
+  constexpr int DK = D / 32;            // MFMA k-steps over head_dim
+  constexpr int KB = NW / 16;           // 16-key blocks per wave
+  constexpr int DB = D / 16;            // 16-wide head_dim blocks of the output
+  static_assert(TCH % (64 * NWAVE) == 0, "tile not divisible among waves");
+  static_assert(NW % 32 == 0 && CH >= 8, "shape");
+
+  // Two K/V buffers as four separate LDS objects: the loop below is unrolled
+  // by two so every access names one fixed buffer, which lets the compiler
+  // see that the direct loads into one buffer cannot alias reads of the other
+  // (it then keeps those loads in flight across the tile's compute).
+  __shared__ uint4 lds_k0[TCH], lds_v0[TCH], lds_k1[TCH], lds_v1[TCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+
+  const WorkItem it = a.work[blockIdx.x];
+  if (it.nrows == 0) return;                    // padding task (whole work group)
+  const ReqInfo rq = a.reqs[it.b];
+  const int G = a.group;
+  const int R = rq.qo_len * G;                  // packed rows of this (request, kv head)
+  const int shift_q = rq.kv_len - rq.qo_len;    // bottom-right offset L - Q
+  const int win = rq.window;
+
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ vp = static_cast<const T*>(a.v);
+
+  // ---- Q fragments (B operand of S^T = K Q^T) and per-row visible ranges
+  frag qf[QB][DK];
+  int lo[QB], hi[QB];
+  int mrow[QB];   // custom mask: bit index of (row, key 0)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = it.row0 + wm * MW + qb * 16 + l16;
+    const bool valid = (r - it.row0) < it.nrows && r < R;
+    mrow[qb] = rq.mask_off * 8;
+    if (valid) {
+      const int pos = r / G;
+      mrow[qb] += pos * rq.kv_len;
+      const int h = it.kvh * G + (r - pos * G);
+      const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk)
+        qf[qb][dk] = __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(src + dk * 32 + g * 8));
+      int l0 = 0;
+      if (win >= 0) l0 = max(0, pos + shift_q - win);
+      const int h0 = a.causal ? pos + shift_q : rq.kv_len - 1;
+      lo[qb] = max(l0, it.key_lo);
+      hi[qb] = min(h0, it.kv_end - 1);
+    } else {
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) qf[qb][dk] = __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0));
+      lo[qb] = 1;
+      hi[qb] = 0;
+    }
+  }
+
+  // Keys every valid row of the task sees: tiles inside need no mask.
+  int full_lo, full_hi;
+  {
+    const int rmax = min(it.row0 + it.nrows, R) - 1;
+    const int pmin = it.row0 / G;
+    const int pmax = rmax / G;
+    full_lo = (win >= 0) ? max(0, pmax + shift_q - win) : 0;
+    full_lo = max(full_lo, it.key_lo);
+    full_hi = a.causal ? pmin + shift_q : rq.kv_len - 1;
+    full_hi = min(full_hi, it.kv_end - 1);
+    if constexpr (kMask) full_hi = min(full_hi, rq.mask_full - 1);
+  }
+
+  f32x4 oacc[DB][QB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int ntiles = it.kv_end > it.tile_begin ? (it.kv_end - it.tile_begin + NWG - 1) / NWG : 0;
+  const int last_key = it.kv_end - 1;
+
+  // Direct global->LDS loads: wave instruction m fills tile slots
+  // [(m * NWAVE + wave) * 64, +64); lane i writes slot +i, which is key row
+  // (m * NWAVE + wave) * RPI + i / CH at position i % CH, i.e. logical chunk
+  // swz_k / swz_v of it.  Keys at or past kv_end read the last key instead
+  // (finite data, masked to zero weight), so no read leaves the request.
+  uint32_t koff[NI], voff[NI];   // element offsets of this lane's chunks within a key row
+  uint32_t kin[NI], vin[NI];     // ... plus the lane's fixed slot (PM 1) or row (PM 3)
+  int lrow[NI];
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    lrow[m] = (m * NWAVE + wave) * RPI + lane / CH;
+    koff[m] = (uint32_t)swz_k<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.k_s_head;
+    voff[m] = (uint32_t)swz_v<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.v_s_head;
+    const uint32_t lslot = PM == 3 ? (uint32_t)(lane / CH)
+                                   : (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
+    kin[m] = lslot * a.k_s_tok + koff[m];
+    vin[m] = lslot * a.v_s_tok + voff[m];
+  }
+  // page (and, on the general path, slot) of each lane row of the next tile
+  uint32_t lpage[NI], lslot[NI];
+  uint32_t spage[NI];       // PM 3: page of each load instruction's rows (scalar)
+  const int32_t* ptab = a.pages + rq.page_off;
+  const const_i32* ptab_s = (const const_i32*)ptab;   // scalar loads
+  auto fetch_pages = [&](int j0) {
+    if constexpr (PM == 3) {
+#pragma unroll
+      for (int m = 0; m < NI; ++m)
+        spage[m] = (uint32_t)ptab_s[(uint32_t)min(j0 + (m * NWAVE + wave) * RPI, last_key) >>
+                                    a.page_shift];
+      return;
+    }
+    if (PM == 1 && j0 + NWG <= it.kv_end) {
+      const int32_t* pt = ptab + (j0 >> a.page_shift);
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        lpage[m] = (uint32_t)pt[lrow[m] >> a.page_shift];
+        lslot[m] = (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const KeyLoc l = locate_key(ptab, (uint32_t)min(j0 + lrow[m], last_key), a.page_magic,
+                                    a.page_shift, (uint32_t)a.page_size);
+        lpage[m] = l.page;
+        lslot[m] = l.slot;
+      }
+    }
+  };
+  auto issue_tile = [&](int j0, uint4* kdst, uint4* vdst) {
+    if constexpr (PM == 3) {
+      // one page per instruction: SGPR base + per-lane 32-bit byte offset
+      const char* kb = reinterpret_cast<const char*>(kp);
+      const char* vb = reinterpret_cast<const char*>(vp);
+      const uint32_t lk = (uint32_t)(uintptr_t)kdst, lv = (uint32_t)(uintptr_t)vdst;
+      const uint32_t pmask = (uint32_t)a.page_size - 1;
+      const bool full = j0 + NWG <= it.kv_end;
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const int rk = j0 + (m * NWAVE + wave) * RPI;
+        const uint32_t lofs = (uint32_t)((m * NWAVE + wave) * 64 * 16);
+        const char* kpg = kb + (uint64_t)spage[m] * a.k_s_page * sizeof(T);
+        const char* vpg = vb + (uint64_t)spage[m] * a.v_s_page * sizeof(T);
+        if (full) {
+          const uint32_t slot0 = (uint32_t)rk & pmask;
+          dma16(kpg + slot0 * a.k_s_tok * sizeof(T), kin[m] * sizeof(T), lk + lofs);
+          dma16(vpg + slot0 * a.v_s_tok * sizeof(T), vin[m] * sizeof(T), lv + lofs);
+        } else {
+          const uint32_t slot = (uint32_t)min(rk + lane / CH, last_key) & pmask;
+          dma16(kpg, (slot * a.k_s_tok + koff[m]) * sizeof(T), lk + lofs);
+          dma16(vpg, (slot * a.v_s_tok + voff[m]) * sizeof(T), lv + lofs);
+        }
+      }
+    } else if (PM == 1 && j0 + NWG <= it.kv_end) {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const uint64_t ko = (uint64_t)lpage[m] * a.k_s_page + kin[m];
+        const uint64_t vo = (uint64_t)lpage[m] * a.v_s_page + vin[m];
+        const int base = (m * NWAVE + wave) * 64;
+        load_lds16(kp + ko, kdst + base);
+        load_lds16(vp + vo, vdst + base);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const KeyLoc l{lpage[m], lslot[m]};
+        const uint64_t ko = key_offset(l, a.k_s_page, a.k_s_tok, koff[m]);
+        const uint64_t vo = key_offset(l, a.v_s_page, a.v_s_tok, voff[m]);
+        const int base = (m * NWAVE + wave) * 64;
+        load_lds16(kp + ko, kdst + base);
+        load_lds16(vp + vo, vdst + base);
+      }
+    }
+  };
+
+  // One LDS tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](auto masked, const uint4* kt, const char* vt, int j0) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x4 s[KB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row = wn * NW + kb * 16 + l16;
+        const frag af = __builtin_bit_cast(frag, kt[row * CH + swz_k<CH>(row, dk * 4 + g)]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(af, qf[qb][dk], s[kb][qb]);
+      }
+    }
+
+    // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
+    const int jl = j0 + wn * NW + 4 * g;
+    // logits soft-cap: scores become cap * log2(e) * tanh(sm_scale * s / cap),
+    // already in log2 units; masked scores are set to -inf after this, below.
+    // tanh(y) is 1 - 2 / (1 + e^{2y}) (exp2 and a reciprocal) for |y| >= 1/4
+    // and its Taylor series y (1 - y^2/3 + 2y^4/15 - 17y^6/315) below, where
+    // the first form would lose the small value to cancellation (relative
+    // error of either below 1e-6, so a large cap reproduces the plain logit).
+    const float mul = kCap ? 1.f : a.scale_log2;
+    if constexpr (kCap) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = s[kb][qb][i] * a.cap_in;
+            const float y2 = y * y;
+            const float series =
+                y * __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2, -17.f / 315.f,
+                                                                         2.f / 15.f),
+                                                      -1.f / 3.f),
+                                   1.f);
+            const float e = fast_exp2(y * 2.8853900817779268f);   // e^{2y}
+            const float big = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
+            s[kb][qb][i] = (fabsf(y) < 0.25f ? series : big) * a.cap_out;
+          }
+    }
+    // Lazy rescaling: exponents are taken against a reference m_run per row
+    // that moves only when a score exceeds it by more than kTau (log2 units),
+    // so every p stays <= 2^kTau; the reference cancels in o = sum p v / sum p
+    // and is added back into lse.  The common case needs no cross-lane work:
+    // each lane tests its own scores against the (row-uniform) reference, and
+    // only when some lane of the wave fails does the wave reduce the row
+    // maxima over the four lane groups of a row and rescale.
+    float mloc[QB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[kb][qb][i];
+          if constexpr (MASKED) {
+            const int j = jl + kb * 16 + i;
+            bool ok = j >= lo[qb] && j <= hi[qb];
+            if constexpr (kMask) {
+              // the key index is clamped into the request so the byte read
+              // stays inside its mask whatever ok is
+              const int bit = mrow[qb] + min(max(j, 0), rq.kv_len - 1);
+              ok = ok && ((a.mask[bit >> 3] >> (bit & 7)) & 1);
+            }
+            x = ok ? x : kNegInf;
+            s[kb][qb][i] = x;
+          }
+          mx = fmaxf(mx, x);
+        }
+      }
+      mloc[qb] = mx * mul;
+      grow = grow || (mloc[qb] > m_run[qb] + kTau);
+    }
+    if (wave_any(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = fmaxf(mloc[qb], __shfl_xor(mloc[qb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][qb][i], mul, -m_use));
+          s[kb][qb][i] = p;
+          rs += p;
+        }
+      }
+      l_run[qb] += rs;
+    }
+
+    // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
+    // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
+    // S^T left them.  The A operand (V^T) comes from two transposing LDS
+    // reads: lane r of each 16-lane group points at 4 head-dim elements
+    // d0 + 4(r%4) of key 4g + r/4 (+16); the read hands lane t element
+    // V[4g + k][d0 + t] as its element k.
+#pragma unroll
+    for (int st = 0; st < NW / 32; ++st) {
+      frag pb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[qb][i] = from_f32<T>(s[2 * st][qb][i]);
+          pb[qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
+        }
+      }
+      const int key0 = wn * NW + st * 32 + 4 * g + (l16 >> 2);
+      const int key1 = key0 + 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 16 + 4 * (l16 & 3);        // first of 4 elements this lane points at
+        const int c = d >> 3, off = (d & 7) * 2;      // chunk and byte offset inside it
+        const int a0 = (key0 * CH + swz_v<CH>(key0, c)) * 16 + off;
+        const int a1 = (key1 * CH + swz_v<CH>(key1, c)) * 16 + off;
+        const frag af = __builtin_bit_cast(frag, lds_read_tr16_x2(vt + a0, vt + a1));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(af, pb[qb], oacc[db][qb]);
+      }
+    }
+  };
+
+  auto run_tile = [&](const uint4* kt, const uint4* vt, int j0) {
+    const char* vtc = reinterpret_cast<const char*>(vt);
+    if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
+      tile(Flag<false>{}, kt, vtc, j0);
+    else
+      tile(Flag<true>{}, kt, vtc, j0);
+  };
+
+  if (ntiles > 0) {
+    fetch_pages(it.tile_begin);
+    issue_tile(it.tile_begin, lds_k0, lds_v0);
+    if (ntiles > 1) fetch_pages(it.tile_begin + NWG);
+  }
+  wait_all();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; t += 2) {
+    const int j0 = it.tile_begin + t * NWG;
+    // even tile: compute from buffer 0 while buffer 1 fills
+    if (t + 1 < ntiles) {
+      issue_tile(j0 + NWG, lds_k1, lds_v1);
+      if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
+    }
+    run_tile(lds_k0, lds_v0, j0);
+    wait_all();
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    // odd tile: compute from buffer 1 while buffer 0 fills
+    if (t + 2 < ntiles) {
+      issue_tile(j0 + 2 * NWG, lds_k0, lds_v0);
+      if (t + 3 < ntiles) fetch_pages(j0 + 3 * NWG);
+    }
+    run_tile(lds_k1, lds_v1, j0 + NWG);
+    wait_all();
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  // Row sums were kept per lane; reduce over the 4 lane groups sharing a row.
+  float l_tot[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float x = l_run[qb] + __shfl_xor(l_run[qb], 16);
+    l_tot[qb] = x + __shfl_xor(x, 32);
+  }
+
+  T* __restrict__ op = static_cast<T*>(a.o);
+  const bool to_partial = it.slot >= 0;
+
+  if constexpr (WN == 1) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int rl = wm * MW + qb * 16 + l16;  // row within the task
+      const int r = it.row0 + rl;
+      if (rl >= it.nrows || r >= R) continue;
+      const float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+      const float lse2 = l_tot[qb] > 0.f ? m_run[qb] + fast_log2(l_tot[qb]) : kNegInf;
+      if (to_partial) {
+        float* dst = a.part_o + ((int64_t)it.slot * (WM * MW) + rl) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          f32x4 v = oacc[db][qb] * inv;
+          *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = v;
+        }
+        if (g == 0) a.part_lse[(int64_t)it.slot * (WM * MW) + rl] = lse2;
+      } else {
+        const int pos = r / G;
+        const int h = it.kvh * G + (r - pos * G);
+        const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+        T* dst = op + orow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          T o4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(oacc[db][qb][i] * inv);
+          *reinterpret_cast<uint2*>(dst + db * 16 + 4 * g) = *reinterpret_cast<uint2*>(o4);
+        }
+        if (g == 0 && a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+    }
+  } else {
+    // Waves along keys hold partial states of the same rows: combine in LDS.
+    static_assert(WM == 1, "key-split tiles use one row block");
+    // per-wave [MW][D] fp32 slices: waves 0..WN/2-1 in lds_k0, the rest in lds_k1
+    auto red_o_of = [&](int w) -> float* {
+      float* base = reinterpret_cast<float*>(w < WN / 2 ? lds_k0 : lds_k1);
+      return base + (w % (WN / 2)) * MW * D;
+    };
+    float* red_m = reinterpret_cast<float*>(lds_v0);     // [WN][MW]
+    float* red_l = red_m + WN * MW;                      // [WN][MW]
+    static_assert(WN % 2 == 0 && (WN / 2) * MW * D * 4 <= (int)sizeof(lds_k0), "LDS too small");
+    static_assert(2 * WN * MW * 4 <= (int)sizeof(lds_v0), "LDS too small");
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (g == 0) {
+        red_m[wn * MW + qb * 16 + l16] = m_run[qb];
+        red_l[wn * MW + qb * 16 + l16] = l_tot[qb];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int rl = qb * 16 + l16;
+      float mt = kNegInf;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) mt = fmaxf(mt, red_m[w * MW + rl]);
+      const float mu = (mt == kNegInf) ? 0.f : mt;
+      const float sc = fast_exp2(m_run[qb] - mu);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x4 v = oacc[db][qb] * sc;
+        *reinterpret_cast<f32x4*>(red_o_of(wn) + rl * D + db * 16 + 4 * g) = v;
+      }
+    }
+    __syncthreads();
+    // Every thread finishes 4 consecutive head-dim elements of some rows.
+    for (int idx = tid; idx < MW * (D / 4); idx += 64 * NWAVE) {
+      const int rl = idx / (D / 4);
+      const int d4 = idx - rl * (D / 4);
+      float mt = kNegInf;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) mt = fmaxf(mt, red_m[w * MW + rl]);
+      const float mu = (mt == kNegInf) ? 0.f : mt;
+      float lt = 0.f;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        lt += red_l[w * MW + rl] * fast_exp2(red_m[w * MW + rl] - mu);
+        acc += *reinterpret_cast<const f32x4*>(red_o_of(w) + rl * D + d4 * 4);
+      }
+      const int r = it.row0 + rl;
+      if (rl >= it.nrows || r >= R) continue;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse2 = lt > 0.f ? mt + fast_log2(lt) : kNegInf;
+      if (to_partial) {
+        float* dst = a.part_o + ((int64_t)it.slot * MW + rl) * D + d4 * 4;
+        *reinterpret_cast<f32x4*>(dst) = acc * inv;
+        if (d4 == 0) a.part_lse[(int64_t)it.slot * MW + rl] = lse2;
+      } else {
+        const int pos = r / G;
+        const int h = it.kvh * G + (r - pos * G);
+        const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+        T o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i] * inv);
+        *reinterpret_cast<uint2*>(op + orow * D + d4 * 4) = *reinterpret_cast<uint2*>(o4);
+        if (d4 == 0 && a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+    }
+  }
+}
+
+template <typename T, int D, int PM, int VAR>
+static hipError_t launch_attention_pm(int tile_kind, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.num_work);
+  switch (tile_kind) {
+    case TILE_PREFILL:
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64, 2, PM, VAR>), grid, dim3(256), 0, s, a);
+      break;
+    case TILE_SHORT16:
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32, 2, PM, VAR>), grid, dim3(256), 0, s, a);
+      break;
+    case TILE_SHORT32:
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32, 2, PM, VAR>), grid, dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D, int VAR>
+static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
+  if (a.num_work == 0) return hipSuccess;
+  const int nwg = tile_keys(tile_kind);
+  const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
+  if (pow2 && a.page_size >= 512 / D) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
+  if (pow2) return launch_attention_pm<T, D, 1, VAR>(tile_kind, a, s);
+  return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);
+}
+
+template <int VAR>
+hipError_t launch_attention_var(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                hipStream_t s) {
+  if (dtype == 1 && head_dim == 128) return launch_attention_t<__bf16, 128, VAR>(tile_kind, a, s);
+  if (dtype == 1 && head_dim == 64) return launch_attention_t<__bf16, 64, VAR>(tile_kind, a, s);
+  if (dtype == 0 && head_dim == 128) return launch_attention_t<_Float16, 128, VAR>(tile_kind, a, s);
+  if (dtype == 0 && head_dim == 64) return launch_attention_t<_Float16, 64, VAR>(tile_kind, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -156,6 +156,13 @@ struct SampleArgs {
 // dtype: 0 fp16, 1 bf16, 2 fp32 (merge_states only).
 hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
                             hipStream_t stream);
+// variants of launch_attention, one per file: custom mask, soft-cap, both
+hipError_t launch_attention_mask(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                 hipStream_t stream);
+hipError_t launch_attention_cap(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                hipStream_t stream);
+hipError_t launch_attention_mask_cap(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                     hipStream_t stream);
 hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a,
                               hipStream_t stream);
 hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,
