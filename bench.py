@@ -239,6 +239,15 @@ def coverage(pk, torch, dev, iters=20):
     capped = W.config2(values=False)
     capped.logits_soft_cap = 50.0
     cases.append(("paged_prefill_b8_softcap50", capped, {}))
+    rng = np.random.default_rng(2560)
+    qo = rng.integers(128, 1024, size=4, endpoint=True)
+    kv = qo + rng.integers(0, 2048, size=4, endpoint=True)
+    cases.append(("prefill_d256_b4_hq16_hkv8", W.build("prefill_d256", qo, kv, 16, 8, 256, 16, True,
+                                                      -1, W.BF16, seed=None, rng=rng, values=False), {}))
+    kv_v = rng.integers(512, 8192, size=16, endpoint=True)
+    cases.append(("verify_d256_b16_hq16_hkv8", W.build("verify_d256", [4] * 16, kv_v, 16, 8, 256, 16,
+                                                      True, -1, W.BF16, seed=None, rng=rng,
+                                                      values=False), {}))
     for ql in (1, 64):
         for wl in (-1, 4095):
             cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",

@@ -135,7 +135,8 @@ pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr
  *   kv_last_page_len[batch]  host; keys on the request's last page, in [1, page_size]
  *                        when it has a page.  kv_len = (pages - 1) * page_size + last.
  *   num_qo_heads / num_kv_heads: q head h reads kv head h / (num_qo_heads / num_kv_heads).
- *   head_dim in {64, 128}; page_size >= 1; causal 0/1 (bottom-right aligned);
+ *   head_dim in {64, 128, 256} (256: prefill tile only); page_size >= 1;
+ *   causal 0/1 (bottom-right aligned);
  *   window_left >= -1 (-1 = no window); sm_scale finite; dtype PKV_FP16 or PKV_BF16.
  *   int_ws / float_ws: device workspaces of at least the sizes pkv_workspace_size
  *   reports.  The plan writes its task list into int_ws (one async copy on
@@ -144,7 +145,7 @@ pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr
  *   with int_ws_bytes = 0 builds a host-only plan (inspectable, not runnable).
  * Refused (no handle is returned, earlier plans stay valid): decreasing indptr,
  *   indptr[0] != 0, last_page_len out of range, negative page ids, head counts
- *   GQA cannot divide, head_dim not 64/128, window_left < -1, a causal request
+ *   GQA cannot divide, head_dim not 64/128/256, window_left < -1, a causal request
  *   with kv_len < qo_len, a request with query rows and no key, a too-small
  *   workspace.
  * On success *out_plan owns a copy of everything it needs; free it with

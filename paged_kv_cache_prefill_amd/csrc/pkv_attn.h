@@ -519,18 +519,23 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 template <typename T, int D, int PM, int VAR>
 static hipError_t launch_attention_pm(int tile_kind, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.num_work);
-  switch (tile_kind) {
-    case TILE_PREFILL:
-      hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64, 2, PM, VAR>), grid, dim3(256), 0, s, a);
-      break;
-    case TILE_SHORT16:
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32, 2, PM, VAR>), grid, dim3(256), 0, s, a);
-      break;
-    case TILE_SHORT32:
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32, 2, PM, VAR>), grid, dim3(256), 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  if constexpr (D == 256) {   // one shape: 4 waves x 16 rows, 32-key tiles, one wave per SIMD
+    if (tile_kind != TILE_PREFILL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 1, 32, 1, PM, VAR>), grid, dim3(256), 0, s, a);
+  } else {
+    switch (tile_kind) {
+      case TILE_PREFILL:
+        hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, 2, 64, 2, PM, VAR>), grid, dim3(256), 0, s, a);
+        break;
+      case TILE_SHORT16:
+        hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 1, 32, 2, PM, VAR>), grid, dim3(256), 0, s, a);
+        break;
+      case TILE_SHORT32:
+        hipLaunchKernelGGL((attn_kernel<T, D, 1, 4, 2, 32, 2, PM, VAR>), grid, dim3(256), 0, s, a);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
@@ -538,7 +543,6 @@ static hipError_t launch_attention_pm(int tile_kind, const AttnArgs& a, hipStrea
 template <typename T, int D, int VAR>
 static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
   if (a.num_work == 0) return hipSuccess;
-  const int nwg = tile_keys(tile_kind);
   const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
   if (pow2 && a.page_size >= 512 / D) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
   if (pow2) return launch_attention_pm<T, D, 1, VAR>(tile_kind, a, s);
@@ -552,6 +556,8 @@ hipError_t launch_attention_var(int tile_kind, int dtype, int head_dim, const At
   if (dtype == 1 && head_dim == 64) return launch_attention_t<__bf16, 64, VAR>(tile_kind, a, s);
   if (dtype == 0 && head_dim == 128) return launch_attention_t<_Float16, 128, VAR>(tile_kind, a, s);
   if (dtype == 0 && head_dim == 64) return launch_attention_t<_Float16, 64, VAR>(tile_kind, a, s);
+  if (dtype == 1 && head_dim == 256) return launch_attention_t<__bf16, 256, VAR>(tile_kind, a, s);
+  if (dtype == 0 && head_dim == 256) return launch_attention_t<_Float16, 256, VAR>(tile_kind, a, s);
   return hipErrorInvalidValue;
 }
 

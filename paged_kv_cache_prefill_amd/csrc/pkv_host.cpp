@@ -230,8 +230,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     return fail(PKV_EGQA,
                 "num_qo_heads: expected a positive multiple of num_kv_heads=%d, given %d", hkv,
                 hq);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_EINVAL, "head_dim: expected 64 or 128, given %d", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PKV_EINVAL, "head_dim: expected 64, 128 or 256, given %d", head_dim);
   if (page_size < 1) return fail(PKV_EINVAL, "page_size: expected >= 1, given %d", page_size);
   if (causal != 0 && causal != 1)
     return fail(PKV_EINVAL, "causal: expected 0 or 1, given %d", causal);
@@ -332,12 +332,14 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
   // ---- tile shape
   int kind;
-  if (o.tile == 1) kind = TILE_PREFILL;
+  if (head_dim == 256 && o.tile == 2)
+    return fail(PKV_EINVAL, "opts.tile: the short-query tile has no head_dim 256 form, given 2");
+  if (o.tile == 1 || head_dim == 256) kind = TILE_PREFILL;
   else if (o.tile == 2) kind = max_rows <= 16 ? TILE_SHORT16 : TILE_SHORT32;
   else kind = max_rows <= 16 ? TILE_SHORT16 : (max_rows <= 32 ? TILE_SHORT32 : TILE_PREFILL);
   S->tile_kind = kind;
-  S->rows = tile_rows(kind);
-  S->keys = tile_keys(kind);
+  S->rows = tile_rows(kind, head_dim);
+  S->keys = tile_keys(kind, head_dim);
   const int MR = S->rows, NK = S->keys, G = S->group;
 
   // ---- row tasks with their visible key ranges

@@ -41,10 +41,16 @@ enum TileKind : int32_t {
   TILE_SHORT32 = 3,   // 4 waves along keys: 32 rows x 128 keys per iteration
 };
 
-inline int tile_rows(int kind) {
+// Rows and keys per tile.  head_dim 256 has only the prefill kind, at 64
+// rows x 32 keys (16 rows per wave keep its accumulators in registers).
+inline int tile_rows(int kind, int head_dim) {
+  if (head_dim == 256) return 64;
   return kind == TILE_PREFILL ? 128 : (kind == TILE_SHORT16 ? 16 : 32);
 }
-inline int tile_keys(int kind) { return kind == TILE_PREFILL ? 64 : 128; }
+inline int tile_keys(int kind, int head_dim) {
+  if (head_dim == 256) return 32;
+  return kind == TILE_PREFILL ? 64 : 128;
+}
 
 // Multiply-shift constants for j / page_size over 0 <= j < 2^31: a power of
 // two 2^l uses (1, l); otherwise m = floor(2^(31+l) / P) + 1 with

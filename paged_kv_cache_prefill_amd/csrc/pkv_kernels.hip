@@ -248,6 +248,10 @@ hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a, 
     hipLaunchKernelGGL((split_merge_kernel<_Float16, 128>), grid, dim3(256), 0, s, a);
   else if (dtype == 0 && head_dim == 64)
     hipLaunchKernelGGL((split_merge_kernel<_Float16, 64>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && head_dim == 256)
+    hipLaunchKernelGGL((split_merge_kernel<__bf16, 256>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 256)
+    hipLaunchKernelGGL((split_merge_kernel<_Float16, 256>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -304,6 +308,10 @@ hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a, hip
     hipLaunchKernelGGL((gather_kernel<_Float16, 128>), grid, dim3(256), 0, s, a);
   else if (dtype == 0 && head_dim == 64)
     hipLaunchKernelGGL((gather_kernel<_Float16, 64>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && head_dim == 256)
+    hipLaunchKernelGGL((gather_kernel<__bf16, 256>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 256)
+    hipLaunchKernelGGL((gather_kernel<_Float16, 256>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

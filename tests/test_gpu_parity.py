@@ -439,3 +439,46 @@ def test_soft_cap_full_size(pk):
     w2.logits_soft_cap = 1e6
     o_b, l_b, _ = run(pk, w2)
     assert np.abs(o_a - o_b).max() <= 1e-2 and np.abs(l_a - l_b).max() <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# head_dim 256 (prefill tile only: 64 rows x 32 keys)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+@pytest.mark.parametrize("page", [1, 3, 16])
+def test_head_dim_256_tiny(pk, dtype, page):
+    rng = np.random.default_rng(page * 31 + (dtype == W.BF16))
+    for (hq, hkv) in ((4, 2), (8, 1)):
+        qo = [int(x) for x in rng.integers(1, 70, size=3)]
+        kv = [q + int(x) for q, x in zip(qo, rng.integers(0, 120, size=3))]
+        for causal, wl in ((True, -1), (False, 10), (True, 40)):
+            w = W.build("d256", qo, kv, hq, hkv, 256, page, causal, wl, dtype,
+                        seed=int(rng.integers(1 << 30)), poison=True)
+            ref_o, ref_lse = oracle_full(w)
+            tensors = device_inputs(w)
+            for chunks in (0, 3):
+                o, lse, p = run(pk, w, tensors, num_kv_chunks=chunks)
+                assert p.info["tile_rows"] == 64 and p.info["tile_keys"] == 32
+                assert_close(o, lse, ref_o, ref_lse, dtype,
+                             f"d256 P={page} h={hq}/{hkv} causal={causal} w={wl} chunks={chunks}")
+
+
+def test_head_dim_256_full_size(pk):
+    rng = np.random.default_rng(2560)
+    qo = rng.integers(128, 1024, size=4, endpoint=True)
+    kv = qo + rng.integers(0, 2048, size=4, endpoint=True)
+    w = W.build("prefill_d256", qo, kv, 16, 8, 256, 16, True, -1, W.BF16, seed=None, rng=rng,
+                poison=True)
+    floats = w.float_inputs()
+    o, lse, _ = run(pk, w)
+    check_sampled(w, o, lse, np.random.default_rng(1), "d256 prefill", floats=floats,
+                  per_request=2, heads=3)
+    w.logits_soft_cap = 50.0
+    o, lse, _ = run(pk, w)
+    check_sampled(w, o, lse, np.random.default_rng(2), "d256 prefill cap 50", floats=floats,
+                  per_request=2, heads=3)
+    kv_v = rng.integers(512, 8192, size=16, endpoint=True)
+    wv = W.build("verify_d256", [4] * 16, kv_v, 16, 8, 256, 16, True, -1, W.BF16, seed=None,
+                 rng=rng, poison=True)
+    o, lse, _ = run(pk, wv)
+    check_sampled(wv, o, lse, np.random.default_rng(3), "d256 verify", per_request=2, heads=3)

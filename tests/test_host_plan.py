@@ -47,6 +47,8 @@ def test_plan_refusals():
     refused("EGQA", num_kv_heads=0)
     refused("EGQA", num_kv_heads=-2)
     refused("EINVAL", head_dim=96)
+    assert pk.plan_host(**{**_base(), "head_dim": 256}).info["tile_rows"] == 64
+    assert "head_dim 256" in refused("EINVAL", head_dim=256, tile=2)
     refused("EINVAL", page_size=0)
     refused("EINVAL", window_left=-2)
     refused("EINVAL", qo_indptr=[1, 4, 10])
