@@ -6,9 +6,10 @@ sampling.py.
 """
 from .attention import (NEG_INF, allowed_mask, append_paged_kv, attention,
                         attention_bruteforce, attention_rows, custom_mask_rows,
-                        gather_request_kv, kv_lengths, merge_many, merge_states, soft_cap)
+                        decode_e4m3, gather_request_kv, kv_lengths, merge_many, merge_states,
+                        soft_cap)
 from .sampling import chain_speculative_sampling, inverse_cdf
 
 __all__ = ["NEG_INF", "allowed_mask", "append_paged_kv", "attention", "attention_bruteforce",
            "attention_rows", "custom_mask_rows", "gather_request_kv", "kv_lengths",
-           "merge_many", "merge_states", "soft_cap", "chain_speculative_sampling", "inverse_cdf"]
+           "merge_many", "merge_states", "soft_cap", "decode_e4m3", "chain_speculative_sampling", "inverse_cdf"]

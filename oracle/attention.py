@@ -17,6 +17,7 @@ matmul / exp / log as the only library steps:
 * ``append_paged_kv``   -- writing new K/V rows into their pages.
 * ``custom_mask_rows``  -- a request's topology mask (tree drafts) from packed bits.
 * ``soft_cap``          -- the logits soft-cap transform.
+* ``decode_e4m3``       -- FP8 E4M3 cache bytes to values (times a per-tensor scale).
 
 Sources (web pages of the AMD-Ecosystem FlashInfer fork):
   [W]  PR #339 "Route non-causal windowed prefill to AITER's masked kernel",
@@ -37,6 +38,9 @@ Sources (web pages of the AMD-Ecosystem FlashInfer fork):
   [S]  PR #362, Architecture / design notes and per-commit messages: a
        logits soft-cap exists and a route that ignores it gives a wrong
        answer (the pages gate on it but do not give the formula).
+  [F]  PR #362, per-commit messages (the merge with the fp8 branch): fp8
+       prefill exists on the in-tree paged route (the pages do not give the
+       format).
 
 Readings where the pages are silent (each also listed in the design notes):
   * kv_len = (n_pages - 1) * page_size + last_page_len, 0 for no pages.
@@ -54,6 +58,9 @@ Readings where the pages are silent (each also listed in the design notes):
     left window still applies on top of it.
   * logits soft-cap [S]: with cap > 0 every scaled logit s becomes
     cap * tanh(s / cap) before the softmax (cap = 0: no cap).
+  * fp8 K/V [F]: the OCP FP8 E4M3 format (sign, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 subnormal; S.1111.111 NaN; no infinities),
+    each cache multiplied by a per-tensor float scale.
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (brute force, closed forms, library routines, invariants, golden fixtures).
 """
@@ -125,6 +132,23 @@ def soft_cap(s, cap):
     if not cap > 0:
         raise ValueError(f"logits_soft_cap: expected >= 0, given {cap}")
     return cap * np.tanh(np.asarray(s, dtype=np.float64) / cap)
+
+
+def decode_e4m3(codes, scale=1.0):
+    """Values of FP8 E4M3 codes (uint8 array), times scale [F].
+
+    value = (-1)^s * 2^(e - 7) * (1 + m / 8) for exponent field e in 1..15
+    (except e = 15, m = 7: NaN), and (-1)^s * 2^-6 * (m / 8) for e = 0.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    normal = np.ldexp(1.0 + m / 8.0, e - 7)
+    sub = np.ldexp(m / 8.0, -6)
+    v = sign * np.where(e == 0, sub, normal)
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return v * float(scale)
 
 
 def custom_mask_rows(custom_mask, mask_indptr, b, qo_len, kv_len):

@@ -673,3 +673,45 @@ def test_soft_cap_bounds_limit_and_bruteforce():
     # and the cap bites: the uncapped scores at that scale differ
     o3, _ = oracle.attention(q, k, v, **big)
     assert np.abs(o3 - o1).max() > 0.1
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 K/V
+# ---------------------------------------------------------------------------
+def test_e4m3_golden_codes():
+    with open(os.path.join(GOLDEN, "e4m3.json")) as f:
+        g = json.load(f)
+    got = oracle.decode_e4m3(np.array(g["codes"], np.uint8))
+    assert np.array_equal(got, np.array(g["values"])), got
+    assert np.signbit(got[1])
+    assert np.isnan(oracle.decode_e4m3(np.array(g["nan_codes"], np.uint8))).all()
+    assert np.array_equal(oracle.decode_e4m3(np.array(g["codes"], np.uint8), 0.5),
+                          np.array(g["values"]) * 0.5)
+
+
+def test_e4m3_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.array_equal(ours[~both_nan], ref[~both_nan])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+
+
+def test_attention_over_e4m3_pools_is_attention_over_their_values():
+    w = W.build("fp8", [5, 9], [33, 40], 4, 2, 16, 8, True, -1, W.BF16, seed=95)
+    rng = np.random.default_rng(96)
+    kc = torch.from_numpy(rng.standard_normal(w.k_pool.shape).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vc = torch.from_numpy(rng.standard_normal(w.v_pool.shape).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q, _, _ = w.float_inputs()
+    a = w.plan_args()
+    del a["head_dim"]
+    kf, vf = oracle.decode_e4m3(kc, 0.25), oracle.decode_e4m3(vc, 3.0)
+    o, lse = oracle.attention(q, kf, vf, **a)
+    o2, lse2 = oracle.attention_bruteforce(q, kf, vf, **a)
+    assert np.allclose(o, o2, atol=1e-12) and np.allclose(lse, lse2, atol=1e-12)
+    # the V scale scales o only; the K scale enters the logits
+    o3, lse3 = oracle.attention(q, kf, oracle.decode_e4m3(vc, 1.0), **a)
+    assert np.allclose(o, 3.0 * o3, atol=1e-12) and np.array_equal(lse, lse3)
