@@ -87,9 +87,9 @@ def attention_flops(w):
     return 4.0 * w.head_dim * w.num_qo_heads * visible_pairs(w)
 
 
-def kv_bytes(w):
-    """K and V rows any row of a request can see, x Hkv x 2 x D x 2 bytes, plus q, o, lse."""
-    elem = 2
+def kv_bytes(w, kv_elem=2):
+    """K and V rows any row of a request can see, x Hkv x 2 x D x kv_elem bytes, plus q, o, lse."""
+    elem = kv_elem
     keys = 0
     for b in range(w.batch_size):
         Q, L = int(w.qo_lens[b]), int(w.kv_lens[b])
@@ -97,7 +97,7 @@ def kv_bytes(w):
         lo = 0 if w.window_left < 0 else max(0, L - Q - w.window_left)
         keys += hi - lo + 1
     kv = keys * w.num_kv_heads * 2 * w.head_dim * elem
-    qo = 2 * w.total_q * w.num_qo_heads * w.head_dim * elem + w.total_q * w.num_qo_heads * 4
+    qo = 2 * w.total_q * w.num_qo_heads * w.head_dim * 2 + w.total_q * w.num_qo_heads * 4
     return kv + qo
 
 
@@ -160,14 +160,16 @@ def cpu_baseline(w, budget_s=20.0):
                       f"host has {os.cpu_count()} logical CPUs"}
 
 
-def _random_pools(w, dev, copies, seed):
-    """Timing-only pools of the workload's shape: N(0, 1) drawn on the device."""
+def _random_pools(w, dev, copies, seed, kv_fp8=False):
+    """Timing-only pools of the workload's shape: N(0, 1) drawn on the device
+    (as E4M3 codes for FP8 caches)."""
     import torch
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+    kdt = torch.float8_e4m3fn if kv_fp8 else dt
     shape = (w.num_pages, w.page_size, w.num_kv_heads, w.head_dim)
-    mk = lambda: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+    mk = lambda: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(kdt)
     q = torch.randn((w.total_q, w.num_qo_heads, w.head_dim), generator=g, device=dev,
                     dtype=torch.float32).to(dt)
     return q, [(mk(), mk()) for _ in range(copies)]
@@ -248,6 +250,9 @@ def coverage(pk, torch, dev, iters=20):
     cases.append(("verify_d256_b16_hq16_hkv8", W.build("verify_d256", [4] * 16, kv_v, 16, 8, 256, 16,
                                                       True, -1, W.BF16, seed=None, rng=rng,
                                                       values=False), {}))
+    fp8 = {"kv_dtype": "fp8_e4m3", "k_scale": 0.5, "v_scale": 2.0}
+    cases.append(("verify_b64_hkv8_fp8kv", W.config4(batch=64, values=False), fp8))
+    cases.append(("paged_prefill_b8_fp8kv", W.config2(values=False), fp8))
     for ql in (1, 64):
         for wl in (-1, 4095):
             cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",
@@ -255,9 +260,10 @@ def coverage(pk, torch, dev, iters=20):
                           {"num_kv_chunks": W.CONFIG5_CHUNKS}))
     for i, (name, w, opts) in enumerate(cases):
         dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
-        nbytes = kv_bytes(w)
+        kv_fp8 = opts.get("kv_dtype") == "fp8_e4m3"
+        nbytes = kv_bytes(w, 1 if kv_fp8 else 2)
         copies = max(1, min(16, -(-512_000_000 // max(nbytes, 1))))
-        q, pools = _random_pools(w, dev, copies, seed=7000 + i)
+        q, pools = _random_pools(w, dev, copies, seed=7000 + i, kv_fp8=kv_fp8)
         p = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
         eager_ms, ms = time_rotating(p, q, pools, iters)
         flops = attention_flops(w)

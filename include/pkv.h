@@ -58,7 +58,7 @@ typedef enum {
   PKV_EWORKSPACE = 7   /* workspace missing or too small */
 } pkv_status;
 
-typedef enum { PKV_FP16 = 0, PKV_BF16 = 1, PKV_FP32 = 2 } pkv_dtype;
+typedef enum { PKV_FP16 = 0, PKV_BF16 = 1, PKV_FP32 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 typedef struct pkv_plan_s* pkv_plan_t;
 
@@ -97,6 +97,16 @@ typedef struct {
      every scaled logit s = sm_scale * q.k becomes cap * tanh(s / cap) before
      the softmax, and lse is taken over the capped logits.  0: no cap. */
   float logits_soft_cap;
+  /* K/V cache format (PR #362, per-commit messages: fp8 prefill on the
+     paged route; the format is the reading taken).  0: the query dtype.
+     PKV_FP8_E4M3: one byte per element, OCP E4M3 (bias 7, no infinities,
+     S.1111.111 NaN); key and value values are code * k_scale and
+     code * v_scale (0 means 1).  Cache strides are then in bytes and must be
+     multiples of 16.  Not combinable with custom_mask or logits_soft_cap
+     (refused).  q and o stay in the pkv_run dtype. */
+  int32_t kv_dtype;
+  float k_scale;
+  float v_scale;
 } pkv_plan_options;
 
 /* Scheduling summary of a plan. */

@@ -37,7 +37,7 @@ PKV_OK, PKV_EINVAL, PKV_ELAYOUT, PKV_EGQA, PKV_EMISMATCH, PKV_ENOTPLANNED, PKV_E
     PKV_EWORKSPACE = range(8)
 _STATUS_NAMES = ["OK", "EINVAL", "ELAYOUT", "EGQA", "EMISMATCH", "ENOTPLANNED", "EHIP",
                  "EWORKSPACE"]
-PKV_FP16, PKV_BF16, PKV_FP32 = 0, 1, 2
+PKV_FP16, PKV_BF16, PKV_FP32, PKV_FP8_E4M3 = 0, 1, 2, 3
 
 
 class PkvError(ValueError):
@@ -54,7 +54,8 @@ class _PlanOptions(ctypes.Structure):
                 ("kv_end", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("reserved", ctypes.c_int32 * 4),
                 ("custom_mask", ctypes.c_void_p), ("mask_indptr", ctypes.c_void_p),
-                ("logits_soft_cap", ctypes.c_float)]
+                ("logits_soft_cap", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -165,11 +166,16 @@ def _ptr_i32(a):
 
 
 def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0, custom_mask=None,
-             mask_indptr=None, logits_soft_cap=0.0):
+             mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     o = _PlanOptions()
     o.num_kv_chunks, o.kv_begin, o.kv_end, o.tile = int(num_kv_chunks), int(kv_begin), \
         int(kv_end), int(tile)
     o.logits_soft_cap = float(logits_soft_cap or 0.0)
+    if kv_dtype is not None:
+        if kv_dtype not in ("fp8_e4m3", PKV_FP8_E4M3) and str(kv_dtype) != "torch.float8_e4m3fn":
+            raise PkvError(PKV_EINVAL, f"kv_dtype: expected None or 'fp8_e4m3', given {kv_dtype!r}")
+        o.kv_dtype = PKV_FP8_E4M3
+        o.k_scale, o.v_scale = float(k_scale), float(v_scale)
     if custom_mask is not None or mask_indptr is not None:
         if custom_mask is None or mask_indptr is None:
             raise PkvError(PKV_EINVAL, "custom_mask and mask_indptr: expected both or neither")
@@ -226,6 +232,7 @@ class Plan:
         self.device = device
         self._int_ws = int_ws
         self._float_ws = float_ws
+        self.kv_fp8 = False
         info = _PlanInfo()
         _check(_lib.pkv_plan_get_info(self._h, ctypes.byref(info)))
         self.info = {name: getattr(info, name) for name, _ in _PlanInfo._fields_}
@@ -280,9 +287,11 @@ class Plan:
             raise PkvError(PKV_ELAYOUT, f"q: expected [rows, heads, head_dim], given {q.dim()}-D")
         if q.stride(2) != 1:
             raise PkvError(PKV_ELAYOUT, f"q: head_dim stride must be 1, given {q.stride(2)}")
-        for name, t in (("q", q), ("paged_k", paged_k), ("paged_v", paged_v)):
-            if t.dtype != self.dtype:
-                raise PkvError(PKV_EMISMATCH, f"{name} dtype: planned {self.dtype}, given {t.dtype}")
+        kv_ok = (torch.uint8, torch.float8_e4m3fn) if self.kv_fp8 else (self.dtype,)
+        for name, t, ok in (("q", q, (self.dtype,)), ("paged_k", paged_k, kv_ok),
+                            ("paged_v", paged_v, kv_ok)):
+            if t.dtype not in ok:
+                raise PkvError(PKV_EMISMATCH, f"{name} dtype: planned {ok[0]}, given {t.dtype}")
             if t.device != self.device:
                 raise PkvError(PKV_EMISMATCH, f"{name} device: planned {self.device}, given {t.device}")
         k = self._cache_view(paged_k, kv_layout)
@@ -366,6 +375,7 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
                             ctypes.byref(handle)))
     p = Plan(handle.value, tdtype, int(head_dim), int(num_qo_heads), int(num_kv_heads),
              int(page_size), dev, int_ws, float_ws)
+    p.kv_fp8 = o.kv_dtype == PKV_FP8_E4M3
     nb = np.diff(kv.astype(np.int64)) if batch > 0 else np.zeros(0, dtype=np.int64)
     lens = np.where(nb > 0, (nb - 1) * int(page_size) + last.astype(np.int64), 0)
     p._kv_total = int(lens.sum())
@@ -375,7 +385,8 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
 def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, num_kv_heads,
          head_dim, page_size, causal, window_left=-1, sm_scale=None, dtype="bf16",
          device="cuda", stream=None, num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
-         custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
+         custom_mask=None, mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None, k_scale=1.0,
+         v_scale=1.0):
     """Validate and schedule a batch; returns a runnable Plan.
 
     Host int arrays: qo_indptr[B+1], kv_indptr[B+1], kv_page_indices[kv_indptr[B]],
@@ -384,26 +395,31 @@ def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, 
     custom_mask (packed uint8 bits) / mask_indptr (int64 byte offsets [B+1]): a
     per-request topology mask for tree drafts, with causal=False (see include/pkv.h).
     logits_soft_cap > 0 caps every scaled logit s to cap * tanh(s / cap).
+    kv_dtype="fp8_e4m3": K/V caches hold E4M3 codes (uint8 or torch.float8_e4m3fn),
+    values code * k_scale and code * v_scale; q and o keep `dtype`.
     """
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
                       device, False, stream,
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
                            tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr,
-                           logits_soft_cap=logits_soft_cap))
+                           logits_soft_cap=logits_soft_cap, kv_dtype=kv_dtype, k_scale=k_scale,
+                           v_scale=v_scale))
 
 
 def plan_host(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
               num_kv_heads, head_dim, page_size, causal, window_left=-1, sm_scale=None,
               dtype="bf16", num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
-              custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
+              custom_mask=None, mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None,
+              k_scale=1.0, v_scale=1.0):
     """Validate and schedule without a device: an inspectable, non-runnable Plan."""
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
                       None, True, None,
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
                            tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr,
-                           logits_soft_cap=logits_soft_cap))
+                           logits_soft_cap=logits_soft_cap, kv_dtype=kv_dtype, k_scale=k_scale,
+                           v_scale=v_scale))
 
 
 def verify_plan(kv_indptr, kv_page_indices, kv_last_page_len, q_len_per_req, num_qo_heads,

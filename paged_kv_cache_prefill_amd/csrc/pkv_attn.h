@@ -30,6 +30,7 @@ template <typename T, int D, int WM, int WN, int QB, int NW, int WPE, int PM, in
 __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   constexpr bool kMask = (VAR & 1) != 0;   // custom topology mask
   constexpr bool kCap = (VAR & 2) != 0;    // logits soft-cap
+  constexpr bool kFp8 = (VAR & 4) != 0;    // FP8 E4M3 K/V (converted into LDS)
   using Tr = Traits<T>;
   using frag = typename Tr::frag;
   constexpr int NWAVE = WM * WN;
@@ -372,6 +373,62 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       tile(Flag<true>{}, kt, vtc, j0);
   };
 
+  if constexpr (kFp8) {
+    // FP8 caches: each thread loads whole 16-byte key-row chunks (16 codes)
+    // through the page table into registers while the current tile runs,
+    // then converts them into the other LDS buffer (two bf16/fp16 chunks,
+    // same swizzled layout), before the barrier that closes the tile.
+    constexpr int C16 = D / 16;                     // 16-byte FP8 chunks per key row
+    constexpr int M8 = NWG * C16 / (64 * NWAVE);    // chunks per thread per tile
+    static_assert(M8 >= 1 && NWG * C16 % (64 * NWAVE) == 0, "fp8 tile split");
+    const uint8_t* kb8 = static_cast<const uint8_t*>(a.k);
+    const uint8_t* vb8 = static_cast<const uint8_t*>(a.v);
+    uint4 kst[M8], vst[M8];
+    auto load8 = [&](int j0) {
+#pragma unroll
+      for (int m = 0; m < M8; ++m) {
+        const int gc = tid + m * 64 * NWAVE;
+        const int row = gc / C16, c16 = gc - (gc / C16) * C16;
+        const KeyLoc l = locate_key(ptab, (uint32_t)min(j0 + row, last_key), a.page_magic,
+                                    a.page_shift, (uint32_t)a.page_size);
+        kst[m] = *reinterpret_cast<const uint4*>(
+            kb8 + key_offset(l, a.k_s_page, a.k_s_tok, (uint32_t)it.kvh * a.k_s_head + c16 * 16));
+        vst[m] = *reinterpret_cast<const uint4*>(
+            vb8 + key_offset(l, a.v_s_page, a.v_s_tok, (uint32_t)it.kvh * a.v_s_head + c16 * 16));
+      }
+    };
+    auto store8 = [&](uint4* kdst, uint4* vdst) {
+#pragma unroll
+      for (int m = 0; m < M8; ++m) {
+        const int gc = tid + m * 64 * NWAVE;
+        const int row = gc / C16, c = 2 * (gc - (gc / C16) * C16);
+        uint4 lo, hi;
+        e4m3x16_to<T>(kst[m], lo, hi);
+        kdst[row * CH + swz_k<CH>(row, c)] = lo;
+        kdst[row * CH + swz_k<CH>(row, c + 1)] = hi;
+        e4m3x16_to<T>(vst[m], lo, hi);
+        vdst[row * CH + swz_v<CH>(row, c)] = lo;
+        vdst[row * CH + swz_v<CH>(row, c + 1)] = hi;
+      }
+    };
+    if (ntiles > 0) {
+      load8(it.tile_begin);
+      store8(lds_k0, lds_v0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      const int j0 = it.tile_begin + t * NWG;
+      if (t + 1 < ntiles) load8(j0 + NWG);
+      run_tile(lds_k0, lds_v0, j0);
+      if (t + 1 < ntiles) store8(lds_k1, lds_v1);
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) load8(j0 + 2 * NWG);
+      run_tile(lds_k1, lds_v1, j0 + NWG);
+      if (t + 2 < ntiles) store8(lds_k0, lds_v0);
+      __syncthreads();
+    }
+  } else {
   if (ntiles > 0) {
     fetch_pages(it.tile_begin);
     issue_tile(it.tile_begin, lds_k0, lds_v0);
@@ -400,6 +457,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     wait_all();
     __syncthreads();
   }
+  }   // FP8 / direct-load paths
 
   // ---- epilogue
   // Row sums were kept per lane; reduce over the 4 lane groups sharing a row.
@@ -419,7 +477,8 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const int rl = wm * MW + qb * 16 + l16;  // row within the task
       const int r = it.row0 + rl;
       if (rl >= it.nrows || r >= R) continue;
-      const float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+      float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+      if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
       const float lse2 = l_tot[qb] > 0.f ? m_run[qb] + fast_log2(l_tot[qb]) : kNegInf;
       if (to_partial) {
         float* dst = a.part_o + ((int64_t)it.slot * (WM * MW) + rl) * D;
@@ -496,7 +555,8 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       }
       const int r = it.row0 + rl;
       if (rl >= it.nrows || r >= R) continue;
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
       const float lse2 = lt > 0.f ? mt + fast_log2(lt) : kNegInf;
       if (to_partial) {
         float* dst = a.part_o + ((int64_t)it.slot * MW + rl) * D + d4 * 4;
@@ -544,6 +604,7 @@ template <typename T, int D, int VAR>
 static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
   if (a.num_work == 0) return hipSuccess;
   const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
+  if constexpr ((VAR & 4) != 0) return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);  // FP8: one path
   if (pow2 && a.page_size >= 512 / D) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
   if (pow2) return launch_attention_pm<T, D, 1, VAR>(tile_kind, a, s);
   return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);

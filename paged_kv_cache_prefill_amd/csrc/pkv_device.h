@@ -112,6 +112,24 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// 16 FP8 E4M3 codes (16 bytes, lowest first) to 16 values of T, returned as
+// two 8-element chunks.  Every E4M3 value is exact in bf16 and fp16.
+template <typename T>
+__device__ __forceinline__ void e4m3x16_to(uint4 in, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  T out[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
+    out[4 * i + 0] = static_cast<T>(a[0]);
+    out[4 * i + 1] = static_cast<T>(a[1]);
+    out[4 * i + 2] = static_cast<T>(b[0]);
+    out[4 * i + 3] = static_cast<T>(b[1]);
+  }
+  lo = *reinterpret_cast<const uint4*>(out);
+  hi = *reinterpret_cast<const uint4*>(out + 8);
+}
 // Loads through this pointer type are scalar (constant address space).
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 // Wait for every outstanding memory operation of this wave.

@@ -53,7 +53,8 @@ pkv_status fail(pkv_status st, const char* fmt, ...) {
 }
 
 const char* dtype_name(int d) {
-  return d == PKV_FP16 ? "fp16" : d == PKV_BF16 ? "bf16" : d == PKV_FP32 ? "fp32" : "unknown";
+  return d == PKV_FP16 ? "fp16" : d == PKV_BF16 ? "bf16" : d == PKV_FP32 ? "fp32"
+       : d == PKV_FP8_E4M3 ? "fp8_e4m3" : "unknown";
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -254,6 +255,17 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   if (!(o.logits_soft_cap >= 0.f) || !std::isfinite(o.logits_soft_cap))
     return fail(PKV_EINVAL, "opts.logits_soft_cap: expected a finite value >= 0, given %g",
                 (double)o.logits_soft_cap);
+  if (o.kv_dtype != 0 && o.kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "opts.kv_dtype: expected 0 (the query dtype) or fp8_e4m3 (%d), given %d",
+                (int)PKV_FP8_E4M3, o.kv_dtype);
+  if (o.kv_dtype == PKV_FP8_E4M3) {
+    if (o.custom_mask || o.logits_soft_cap > 0.f)
+      return fail(PKV_EINVAL, "opts.kv_dtype: fp8_e4m3 caches take no custom mask or soft-cap");
+    for (float sc : {o.k_scale, o.v_scale})
+      if (!(sc >= 0.f) || !std::isfinite(sc))
+        return fail(PKV_EINVAL, "opts.k_scale / v_scale: expected finite values >= 0, given %g",
+                    (double)sc);
+  }
   const int64_t opt_end = o.kv_end < 0 ? INT64_MAX : o.kv_end;
 
   const int32_t qi0 = batch > 0 ? qo_indptr[0] : 0;
@@ -548,6 +560,8 @@ struct pkv_plan_s {
   pkv_dtype dtype;
   float sm_scale;
   float soft_cap = 0.f;
+  bool kv_fp8 = false;
+  float k_scale = 1.f, v_scale = 1.f;
   uint32_t page_magic = 1, page_shift = 0;
   uint8_t* int_ws = nullptr;
   float* float_ws = nullptr;
@@ -603,6 +617,11 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
   p->dtype = dtype;
   p->sm_scale = sm_scale;
   p->soft_cap = opts ? opts->logits_soft_cap : 0.f;
+  if (opts && opts->kv_dtype == PKV_FP8_E4M3) {
+    p->kv_fp8 = true;
+    p->k_scale = opts->k_scale > 0.f ? opts->k_scale : 1.f;
+    p->v_scale = opts->v_scale > 0.f ? opts->v_scale : 1.f;
+  }
   page_divider((uint32_t)page_size, &p->page_magic, &p->page_shift);
   const bool dry = (int_ws == nullptr && int_ws_bytes == 0);
   if (!dry) {
@@ -709,11 +728,12 @@ pkv_status check_cache(const pkv_plan_s* p, const char* name, const void* ptr, i
   if (S.total_kv > 0 && !ptr) return fail(PKV_EINVAL, "%s: expected a device pointer, given NULL", name);
   if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
     return fail(PKV_ELAYOUT, "%s: expected 16-byte alignment", name);
-  if (s_page < 0 || s_tok < 0 || s_head < 0 || s_page % 8 || s_tok % 8 || s_head % 8)
+  const int g = p->kv_fp8 ? 16 : 8;   // elements per 16 bytes
+  if (s_page < 0 || s_tok < 0 || s_head < 0 || s_page % g || s_tok % g || s_head % g)
     return fail(PKV_ELAYOUT,
                 "%s strides (page %lld, token %lld, head %lld): expected non-negative multiples "
-                "of 8 elements with a packed head_dim",
-                name, (long long)s_page, (long long)s_tok, (long long)s_head);
+                "of %d elements with a packed head_dim",
+                name, (long long)s_page, (long long)s_tok, (long long)s_head, g);
   // the kernels address a key as page * s_page (64-bit) + an in-page offset (32-bit)
   const int64_t in_page = (int64_t)(psize - 1) * s_tok + (int64_t)(heads - 1) * s_head + dim;
   if (s_page >= (1ll << 31) || in_page >= (1ll << 31))
@@ -805,7 +825,9 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   a.page_magic = p->page_magic;
   a.page_shift = p->page_shift;
   a.causal = S.causal;
-  a.scale_log2 = p->sm_scale * 1.4426950408889634f;
+  a.scale_log2 = p->sm_scale * 1.4426950408889634f * (p->kv_fp8 ? p->k_scale : 1.f);
+  a.kv_fp8 = p->kv_fp8 ? 1 : 0;
+  a.v_scale = p->v_scale;
   a.cap_in = p->soft_cap > 0.f ? p->sm_scale / p->soft_cap : 0.f;
   a.cap_out = p->soft_cap > 0.f ? p->soft_cap * 1.4426950408889634f : 0.f;
   hipError_t e = launch_attention(S.tile_kind, (int)p->dtype, S.head_dim, a, hs);
@@ -974,6 +996,7 @@ pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_
   if (!p) return fail(PKV_ENOTPLANNED, "plan: debug_gather before a successful plan");
   if (!p->has_device_copy)
     return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
+  if (p->kv_fp8) return fail(PKV_EINVAL, "debug_gather: fp8_e4m3 caches are not gathered");
   const Schedule& S = p->S;
   if (dtype != p->dtype)
     return fail(PKV_EMISMATCH, "dtype: planned %s, given %s", dtype_name(p->dtype),

@@ -98,6 +98,8 @@ struct AttnArgs {
   // = cap * log2(e) * tanh(sm_scale * raw / cap); cap_out = 0: no cap
   float cap_in;            // sm_scale / cap
   float cap_out;           // cap * log2(e)
+  int32_t kv_fp8;          // 1: K/V are FP8 E4M3 codes (k_scale folded into scale_log2)
+  float v_scale;           // FP8 V: value = code * v_scale
 };
 
 struct SplitMergeArgs {
@@ -169,6 +171,8 @@ hipError_t launch_attention_cap(int tile_kind, int dtype, int head_dim, const At
                                 hipStream_t stream);
 hipError_t launch_attention_mask_cap(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
                                      hipStream_t stream);
+hipError_t launch_attention_fp8(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                hipStream_t stream);
 hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a,
                               hipStream_t stream);
 hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,

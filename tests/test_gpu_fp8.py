@@ -1,0 +1,103 @@
+"""FP8 E4M3 K/V caches on the GPU against the oracle (values = code x scale,
+decoded by the oracle from the format's definition): every head dim, page
+address path and tile shape, windows, split chunks, NaN-poisoned unreferenced
+codes, full-size verify and prefill on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import O_TOL, LSE_TOL, assert_close, require_gpu, to_device, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+KS, VS = 0.5, 2.0
+
+
+@pytest.fixture(scope="module")
+def pk():
+    return require_gpu()
+
+
+def _run(pk, w, kc, vc, **opts):
+    q = to_device(w.q, w.dtype)
+    k = torch.from_numpy(kc).cuda()
+    v = torch.from_numpy(vc).cuda()
+    p = pk.plan(**w.plan_args(), dtype=torch_dtype(w.dtype), kv_dtype="fp8_e4m3", k_scale=KS,
+                v_scale=VS, **opts)
+    o, lse = p.run(q, k, v)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), p
+
+
+def _floats(w, kc, vc):
+    q, _, _ = w.float_inputs()
+    return q, oracle.decode_e4m3(kc, KS), oracle.decode_e4m3(vc, VS)
+
+
+def _oracle(w, kc, vc):
+    q, k, v = _floats(w, kc, vc)
+    a = w.plan_args()
+    del a["head_dim"]
+    return oracle.attention(q, k, v, **a)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("page", [1, 3, 16])
+def test_fp8_tiny(pk, d, page):
+    rng = np.random.default_rng(d * 10 + page)
+    qo = [1, 23, 70]
+    kv = [40, 23, 190]
+    for causal, wl in ((True, -1), (False, 12), (True, 60)):
+        w = W.build("fp8", qo, kv, 8, 2, d, page, causal, wl, W.BF16,
+                    seed=int(rng.integers(1 << 30)))
+        kc, vc = W.e4m3_pools(w, int(rng.integers(1 << 30)), KS, VS)
+        ref_o, ref_lse = _oracle(w, kc, vc)
+        for tile in ((1,) if d == 256 else (1, 2)):
+            for chunks in (0, 3):
+                o, lse, _ = _run(pk, w, kc, vc, tile=tile, num_kv_chunks=chunks)
+                assert_close(o, lse, ref_o, ref_lse, w.dtype,
+                             f"fp8 d={d} P={page} causal={causal} w={wl} tile={tile} "
+                             f"chunks={chunks}")
+
+
+def test_fp8_fp16_queries(pk):
+    w = W.build("fp8h", [17, 5], [90, 300], 8, 4, 128, 16, True, -1, W.FP16, seed=5)
+    kc, vc = W.e4m3_pools(w, 6, KS, VS)
+    ref_o, ref_lse = _oracle(w, kc, vc)
+    o, lse, _ = _run(pk, w, kc, vc)
+    assert_close(o, lse, ref_o, ref_lse, w.dtype, "fp8 with fp16 q")
+
+
+@pytest.mark.parametrize("case", ["verify_b64", "prefill_b8"])
+def test_fp8_full_size(pk, case):
+    w = W.config4(batch=64, num_kv_heads=8, values=True) if case == "verify_b64" else \
+        W.config2(values=True)
+    kc, vc = W.e4m3_pools(w, 77, KS, VS)
+    o, lse, _ = _run(pk, w, kc, vc)
+    floats = _floats(w, kc, vc)
+    rng = np.random.default_rng(8)
+    a = w.plan_args()
+    del a["head_dim"]
+    for b in rng.choice(w.batch_size, size=min(6, w.batch_size), replace=False):
+        ql = int(w.qo_lens[b])
+        rows = sorted({0, ql - 1, int(rng.integers(ql))})
+        heads = [0, 31, int(rng.integers(32))]
+        ref_o, ref_lse = oracle.attention_rows(*floats, **a, b=int(b), rows=rows, heads=heads)
+        base = int(w.qo_indptr[b])
+        go = o[np.ix_([base + r for r in rows], heads)]
+        gl = lse[np.ix_([base + r for r in rows], heads)]
+        assert_close(go, gl, ref_o, ref_lse, w.dtype, f"fp8 {case} b={b}")
+
+
+def test_fp8_refusals(pk):
+    w = W.build("fp8r", [3], [20], 4, 2, 64, 16, True, -1, W.BF16, seed=9)
+    p = pk.plan(**w.plan_args(), dtype=torch.bfloat16, kv_dtype="fp8_e4m3")
+    q = to_device(w.q, w.dtype)
+    kb = to_device(w.k_pool, w.dtype)
+    with pytest.raises(pk.PkvError, match="dtype"):
+        p.run(q, kb, kb)
+    with pytest.raises(pk.PkvError, match="debug_gather|fp8"):
+        kc, vc = W.e4m3_pools(w, 1)
+        p.debug_gather(torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda())

@@ -306,3 +306,39 @@ def spec_sampling_inputs(variant=0, batch=64, num_spec=4, vocab=128256, spread=3
     return dict(draft_probs=draft, draft_token_ids=ids.astype(np.int32), target_probs=target,
                 accept_u=rng.random((batch, num_spec), dtype=np.float32),
                 sample_u=rng.random(batch, dtype=np.float32))
+
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 caches (input encoding only)
+# ----------------------------------------------------------------------------
+
+E4M3_NAN = np.uint8(0x7F)
+
+
+def e4m3_codes(values):
+    """Round float32 values to FP8 E4M3 codes (uint8) with torch's encoder."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_pools(w, seed, scale_k=1.0, scale_v=1.0, poison=True):
+    """K/V pools of w's shape as E4M3 codes of N(0, 1) / scale (so that code *
+    scale is N(0, 1)-like); NaN codes in unreferenced pages and past each
+    request's last key when poisoned."""
+    rng = np.random.default_rng(seed)
+    shape = (w.num_pages, w.page_size, w.num_kv_heads, w.head_dim)
+    k = e4m3_codes(rng.standard_normal(shape, dtype=np.float32) / np.float32(scale_k))
+    v = e4m3_codes(rng.standard_normal(shape, dtype=np.float32) / np.float32(scale_v))
+    if poison:
+        used = np.zeros(w.num_pages, dtype=bool)
+        used[w.kv_page_indices] = True
+        for pool in (k, v):
+            pool[~used] = E4M3_NAN
+            for b in range(w.batch_size):
+                if int(w.kv_indptr[b + 1] - w.kv_indptr[b]) == 0:
+                    continue
+                last_page = int(w.kv_page_indices[w.kv_indptr[b + 1] - 1])
+                pool[last_page, int(w.kv_last_page_len[b]):] = E4M3_NAN
+    return k, v
