@@ -37,8 +37,19 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "masked-attention TFLOP/s (prefill) + KV HBM GB/s (verify), fraction of peak"
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_prefill_amd", "csrc", "pkv_kernels.hip")
+# the files that define the prefill attention kernel; their joint hash tags the
+# committed HBM counters
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_prefill_amd", "csrc", f)
+                  for f in ("pkv_attn.h", "pkv_device.h", "pkv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_paged_b8_hbm.txt")
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -52,9 +63,7 @@ def measured_traffic():
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     rec[k.strip()] = v.strip()
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha:
+        if rec.get("kernel_source_sha256") != kernel_source_sha():
             return None
         return float(rec["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
