@@ -204,7 +204,8 @@ def _plan_arrays(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len):
 
 
 def workspace_size(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
-                   num_kv_heads, head_dim, page_size, causal, window_left=-1, **opts):
+                   num_kv_heads, head_dim, page_size, causal, window_left=-1, sm_scale=None,
+                   **opts):
     """(int workspace bytes, float workspace bytes) a plan with these arguments needs."""
     lib = load_library()
     qo, kv, idx, last, batch = _plan_arrays(qo_indptr, kv_indptr, kv_page_indices,

@@ -507,6 +507,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
 // ---- pinned staging buffers for the one host-to-device copy per plan --------
 struct Staging {
   void* host = nullptr;
+  void* dev_view = nullptr;   // the same pinned memory as the device addresses it
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   int device = -1;
@@ -536,6 +537,12 @@ pkv_status copy_to_device(void* dst, const std::vector<uint8_t>& src, hipStream_
       delete s;
       return fail(PKV_EHIP, "hipHostMalloc(%zu): %s", src.size(), hipGetErrorString(e));
     }
+    e = hipHostGetDevicePointer(&s->dev_view, s->host, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(s->host);
+      delete s;
+      return fail(PKV_EHIP, "hipHostGetDevicePointer: %s", hipGetErrorString(e));
+    }
     e = hipEventCreateWithFlags(&s->ev, hipEventDisableTiming);
     if (e != hipSuccess) {
       (void)hipHostFree(s->host);
@@ -545,12 +552,64 @@ pkv_status copy_to_device(void* dst, const std::vector<uint8_t>& src, hipStream_
     g_staging.push_back(s);
   }
   std::memcpy(s->host, src.data(), src.size());
-  e = hipMemcpyAsync(dst, s->host, src.size(), hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return fail(PKV_EHIP, "hipMemcpyAsync(plan): %s", hipGetErrorString(e));
+  // src.size() is a multiple of 256 (the workspace layout is 256-byte aligned)
+  e = launch_upload(dst, s->dev_view, src.size(), stream);
+  if (e != hipSuccess) return fail(PKV_EHIP, "plan upload launch: %s", hipGetErrorString(e));
   e = hipEventRecord(s->ev, stream);
   if (e != hipSuccess) return fail(PKV_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
   s->in_flight = true;
   return PKV_OK;
+}
+
+// The schedule pkv_workspace_size computed, kept for the pkv_plan call that
+// normally follows it with the same arguments (callers size the workspaces,
+// then plan): that call takes it instead of scheduling again.  It is handed
+// over once and dropped by the next call of either function, so nothing is
+// reused across plans.
+struct PendingSchedule {
+  std::vector<uint8_t> key;   // every input the scheduler reads, serialized
+  Schedule S;
+  bool valid = false;
+};
+thread_local PendingSchedule g_pending;
+
+template <typename X>
+void put(std::vector<uint8_t>& k, const X* p, size_t n) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
+  if (n) k.insert(k.end(), b, b + n * sizeof(X));
+}
+
+// Serialized scheduler inputs; empty when the arrays cannot be read (the
+// scheduler reports those errors itself).
+std::vector<uint8_t> schedule_key(const int32_t* qo, const int32_t* kv, const int32_t* idx,
+                                  const int32_t* last, int32_t batch, int32_t hq, int32_t hkv,
+                                  int32_t head_dim, int32_t page_size, int32_t causal,
+                                  int32_t window_left, const pkv_plan_options* opts) {
+  std::vector<uint8_t> k;
+  if (batch < 0 || (batch > 0 && (!qo || !kv || !last))) return k;
+  const int32_t sc[8] = {batch, hq, hkv, head_dim, page_size, causal, window_left, 0};
+  put(k, sc, 8);
+  if (batch > 0) {
+    put(k, qo, (size_t)batch + 1);
+    put(k, kv, (size_t)batch + 1);
+    put(k, last, (size_t)batch);
+    const int64_t n = kv[batch] - kv[0];
+    if (n < 0 || (n > 0 && !idx)) return {};
+    put(k, idx, (size_t)n);
+  }
+  if (opts) {
+    pkv_plan_options o = *opts;
+    o.custom_mask = nullptr;
+    o.mask_indptr = nullptr;
+    put(k, &o, 1);
+    if (opts->custom_mask && opts->mask_indptr && batch > 0) {
+      put(k, opts->mask_indptr, (size_t)batch + 1);
+      const int64_t bytes = opts->mask_indptr[batch];
+      if (bytes < 0) return {};
+      put(k, opts->custom_mask, (size_t)bytes);
+    }
+  }
+  return k;
 }
 
 }  // namespace
@@ -581,6 +640,7 @@ pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr
                               int32_t window_left, const pkv_plan_options* opts,
                               size_t* int_ws_bytes, size_t* float_ws_bytes) {
   g_err.clear();
+  g_pending.valid = false;
   Schedule S;
   pkv_status st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
                            num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
@@ -588,6 +648,13 @@ pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr
   if (st != PKV_OK) return st;
   if (int_ws_bytes) *int_ws_bytes = S.int_bytes;
   if (float_ws_bytes) *float_ws_bytes = S.float_bytes;
+  g_pending.key = schedule_key(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len,
+                               batch_size, num_qo_heads, num_kv_heads, head_dim, page_size, causal,
+                               window_left, opts);
+  if (!g_pending.key.empty()) {
+    g_pending.S = std::move(S);
+    g_pending.valid = true;
+  }
   return PKV_OK;
 }
 
@@ -606,9 +673,21 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
   if (!std::isfinite(sm_scale))
     return fail(PKV_EINVAL, "sm_scale: expected a finite value, given %g", (double)sm_scale);
   pkv_plan_s* p = new pkv_plan_s();
-  pkv_status st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
-                           num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
-                           opts, &p->S);
+  pkv_status st = PKV_OK;
+  bool reused = false;
+  if (g_pending.valid) {
+    g_pending.valid = false;
+    if (schedule_key(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
+                     num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
+                     opts) == g_pending.key) {
+      p->S = std::move(g_pending.S);
+      reused = true;
+    }
+  }
+  if (!reused)
+    st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
+                  num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left, opts,
+                  &p->S);
   if (st != PKV_OK) {
     delete p;
     return st;

@@ -182,6 +182,8 @@ hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,
 hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a,
                                hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// bytes (a multiple of 16) from device-visible pinned host memory to device memory
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_spec_sample(const SampleArgs& a, hipStream_t stream);
 
 }  // namespace pkv

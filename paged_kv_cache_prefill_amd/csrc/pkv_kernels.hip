@@ -174,6 +174,19 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// plan upload: the task list from pinned host memory into the int workspace
+// ---------------------------------------------------------------------------
+// A kernel on the caller's stream rather than a DMA-engine copy: the next
+// attention launch then follows it on the same queue with no cross-engine
+// synchronisation.  16 bytes per thread; the host pads to a multiple of 16.
+__global__ __launch_bounds__(256) void upload_kernel(uint4* __restrict__ dst,
+                                                     const uint4* __restrict__ src, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
 // append: new K/V rows into their pages
 // ---------------------------------------------------------------------------
 // One thread per (token, head, 16-byte chunk); every index is range-checked
@@ -288,6 +301,15 @@ hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a, c
   if (dtype == 2)
     return launch_merge_t<float>(o_a, lse_a, o_b, lse_b, o_out, lse_out, rh, head_dim, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024;
+  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
