@@ -304,7 +304,9 @@ def time_sampling(pk, torch, dev, iters):
     V = inp["target_probs"].shape[2]
     args = (t["draft_probs"], t["draft_token_ids"], t["target_probs"], t["accept_u"],
             t["sample_u"])
-    out, acc = pk.chain_speculative_sampling(*args)
+    ws = torch.empty(pk.load_library().pkv_chain_speculative_sampling_workspace_size(B, V),
+                     dtype=torch.uint8, device=dev)
+    out, acc = pk.chain_speculative_sampling(*args, workspace=ws)
     torch.cuda.synchronize()
     acc_h = acc.cpu().numpy().astype(np.int64)
     examined = np.minimum(acc_h + 1, n)
@@ -313,7 +315,7 @@ def time_sampling(pk, torch, dev, iters):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for _ in range(4):
-            pk.chain_speculative_sampling(*args, out=out, num_accepted=acc)
+            pk.chain_speculative_sampling(*args, out=out, num_accepted=acc, workspace=ws)
     g.replay()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()

@@ -261,8 +261,13 @@ pkv_status pkv_append_kv(const void* append_k, int64_t ak_s_tok, int64_t ak_s_he
  *   rejected, never read).
  *   output_token_ids [batch][n + 1]: device int32, the accepted drafts, the
  *   drawn token, then -1; num_accepted [batch]: device int32.
+ *   workspace: device scratch of at least
+ *   pkv_chain_speculative_sampling_workspace_size(batch, vocab) bytes,
+ *   16-byte aligned, not read before it is written; calls that share a
+ *   workspace must be ordered on one stream.
  * Refused on the host: batch < 0, n < 0, vocab outside [1, 2^20], NULL
- * pointers when batch > 0, pointers not 4-byte aligned.
+ * pointers when batch > 0, pointers not 4-byte aligned, a small or
+ * unaligned workspace.
  */
 pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
                                           const int32_t* draft_token_ids,
@@ -270,7 +275,12 @@ pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
                                           const float* sample_u, int32_t batch,
                                           int32_t num_speculate_tokens, int32_t vocab_size,
                                           int32_t* output_token_ids, int32_t* num_accepted,
+                                          void* workspace, size_t workspace_bytes,
                                           void* stream);
+
+/* Device workspace bytes pkv_chain_speculative_sampling needs (per-tile sums
+   of the drawn rows): batch * ceil(vocab / 1024) * 16.  Host-only. */
+size_t pkv_chain_speculative_sampling_workspace_size(int32_t batch_size, int32_t vocab_size);
 
 /*
  * debug_gather: write the logical K and V rows of every planned request,

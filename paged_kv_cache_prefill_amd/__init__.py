@@ -105,7 +105,9 @@ def load_library():
                                   vp, i64, i32, i64, i64, i64,
                                   ctypes.c_int, vp, vp]
     lib.pkv_chain_speculative_sampling.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp,
-                                                   vp]
+                                                   vp, sz, vp]
+    lib.pkv_chain_speculative_sampling_workspace_size.argtypes = [i32, i32]
+    lib.pkv_chain_speculative_sampling_workspace_size.restype = sz
     lib.pkv_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.pkv_plan_get_work.argtypes = [vp, pi32, i64, ctypes.POINTER(i64)]
     lib.pkv_plan_destroy.argtypes = [vp]
@@ -523,7 +525,7 @@ def append_kv(append_k, append_v, batch_indices, positions, kv_indptr, kv_page_i
 
 
 def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accept_u, sample_u,
-                               out=None, num_accepted=None, stream=None):
+                               out=None, num_accepted=None, workspace=None, stream=None):
     """Accept/reject each request's draft chain -> (output_token_ids [B, n+1] int32,
     num_accepted [B] int32).
 
@@ -550,10 +552,14 @@ def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accep
         out = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = lib.pkv_chain_speculative_sampling_workspace_size(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     _check(lib.pkv_chain_speculative_sampling(
         draft_probs.data_ptr(), draft_token_ids.data_ptr(), target_probs.data_ptr(),
         accept_u.data_ptr(), sample_u.data_ptr(), B, n, V, out.data_ptr(),
-        num_accepted.data_ptr(), ctypes.c_void_p(stream.cuda_stream)))
+        num_accepted.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        ctypes.c_void_p(stream.cuda_stream)))
     return out, num_accepted

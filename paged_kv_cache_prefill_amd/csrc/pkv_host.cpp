@@ -1030,6 +1030,7 @@ pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
                                           const float* sample_u, int32_t batch,
                                           int32_t num_speculate_tokens, int32_t vocab_size,
                                           int32_t* output_token_ids, int32_t* num_accepted,
+                                          void* workspace, size_t workspace_bytes,
                                           void* stream) {
   g_err.clear();
   if (batch < 0) return fail(PKV_EINVAL, "batch_size: expected >= 0, given %d", batch);
@@ -1059,9 +1060,20 @@ pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
   a.batch = batch;
   a.num_spec = num_speculate_tokens;
   a.vocab = vocab_size;
-  hipError_t e = launch_spec_sample(a, static_cast<hipStream_t>(stream));
+  const size_t need = spec_sample_workspace_bytes(batch, vocab_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EWORKSPACE, "workspace: expected >= %zu bytes, given %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(PKV_ELAYOUT, "workspace: expected 16-byte alignment");
+  hipError_t e = launch_spec_sample(a, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_EHIP, "speculative sampling launch: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+
+size_t pkv_chain_speculative_sampling_workspace_size(int32_t batch_size, int32_t vocab_size) {
+  if (batch_size <= 0 || vocab_size <= 0) return 0;
+  return spec_sample_workspace_bytes(batch_size, vocab_size);
 }
 
 pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_t k_page_size,

@@ -184,6 +184,7 @@ hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a,
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // bytes (a multiple of 16) from device-visible pinned host memory to device memory
 hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream);
-hipError_t launch_spec_sample(const SampleArgs& a, hipStream_t stream);
+size_t spec_sample_workspace_bytes(int32_t batch, int32_t vocab);
+hipError_t launch_spec_sample(const SampleArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace pkv

@@ -11,12 +11,14 @@
 // uniform s per request: the smallest k whose running weight sum exceeds
 // s * total, else the last k with a positive weight.
 //
-// One 1024-thread work group per request.  The accept loop reads two floats
-// per position.  The selected row is read once in tiles of 1024 elements
-// (lane-contiguous, so loads coalesce): each tile's weight sum goes to LDS;
-// one wave then scans the tile sums, finds the tile holding the threshold,
-// and the work group rescans that one tile to find the element.  HBM-bound:
-// the bytes are the selected row(s), 4 or 8 bytes per vocabulary entry.
+// Two kernels.  The first spreads each request's row over many work groups:
+// each redoes the (cheap) accept loop, then sums its share of the row's
+// 1024-entry tiles -- residual and plain weights, and the last positive
+// entry of each -- into the workspace (work group 0 of a request also writes
+// the accepted tokens).  The second, one 1024-thread work group per request,
+// scans the tile sums in order, finds the tile holding s * total, rescans
+// that tile and writes the drawn token.  HBM-bound: the bytes are the row(s)
+// read once, 4 or 8 bytes per vocabulary entry.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -26,8 +28,10 @@
 
 namespace pkv {
 
-constexpr int kSampThreads = 1024;
-constexpr int kSampUnroll = 32;       // tiles whose loads are in flight together
+constexpr int kTile = 1024;           // entries per tile
+constexpr int kSumThreads = 256;      // work group of the tile-sum kernel
+constexpr int kSumUnroll = 8;         // tiles whose loads are in flight together
+constexpr int kDrawThreads = 1024;    // work group of the draw kernel
 constexpr int kSampMaxTiles = 1024;   // vocabulary up to 2^20 entries
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -35,58 +39,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-
-// Weights of U entries k0, k0 + 1024, ... of the row: p, or the residual
-// max(p - q, 0) when qrow is set; entries past the row are 0.  The reads are
-// clamped into the row rather than guarded, so all of them are in flight at
-// once (a guarded read would make the compiler wait for each in turn).
-template <int U>
-__device__ __forceinline__ void row_weights(const float* prow, const float* qrow, int k0, int V,
-                                            float (&w)[U]) {
-  if (qrow != nullptr) {
-    float qv[U];
+__device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kc = min(k0 + u * kSampThreads, V - 1);
-      w[u] = prow[kc];
-      qv[u] = qrow[kc];
-    }
-    // issue every read before using any (the compiler would otherwise start
-    // subtracting, and waiting, after the first pair)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = fmaxf(w[u] - qv[u], 0.f);
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = prow[min(k0 + u * kSampThreads, V - 1)];
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (k0 + u * kSampThreads >= V) w[u] = 0.f;
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
 }
 
-__global__ __launch_bounds__(kSampThreads) void spec_sample_kernel(SampleArgs a) {
-  constexpr int NW = kSampThreads / 64;
-  __shared__ float tile_sum[kSampMaxTiles];
-  __shared__ float wsum[kSampUnroll][NW];
-  __shared__ int lastpos, found, tile_last, tile_s;
-  __shared__ float thr_s, excl_s;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Accept loop of request b: the number of accepted drafts.  Eight positions
+// at a time: ids first, then their probabilities, so the loads overlap.
+// Reads are clamped into the arrays; an id outside the vocabulary is
+// rejected.  With `write`, thread 0 stores the accepted ids.
+__device__ int accept_chain(const SampleArgs& a, int b, bool write) {
   const int n = a.num_spec, V = a.vocab;
   const float* q_b = a.draft_probs + (int64_t)b * n * V;
   const float* p_b = a.target_probs + (int64_t)b * (n + 1) * V;
-  int* out = a.out_ids + (int64_t)b * (n + 1);
-
-  // ---- accept loop (every thread walks it; the reads are shared).  Eight
-  // positions at a time: ids first, then their probabilities, so the loads
-  // overlap instead of forming a chain.
   int t = 0;
   for (int t0 = 0; t0 < n; t0 += 8) {
     int xs[8];
     float ps[8], qs[8], us[8];
-    // reads clamped into the arrays (see row_weights); invalid ones are masked after
 #pragma unroll
     for (int i = 0; i < 8; ++i) xs[i] = a.draft_ids[(int64_t)b * n + min(t0 + i, n - 1)];
 #pragma unroll
@@ -96,60 +66,145 @@ __global__ __launch_bounds__(kSampThreads) void spec_sample_kernel(SampleArgs a)
       ps[i] = p_b[(int64_t)ti * V + xc];
       qs[i] = q_b[(int64_t)ti * V + xc];
       us[i] = a.accept_u[(int64_t)b * n + ti];
-      if (xs[i] < 0 || xs[i] >= V) ps[i] = 0.f;   // an id outside the vocabulary is rejected
+      if (xs[i] < 0 || xs[i] >= V) ps[i] = 0.f;
     }
     int acc = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (acc != i || t0 + i >= n || !(us[i] * qs[i] < ps[i])) continue;
-      if (tid == 0) out[t0 + i] = xs[i];
+      if (write && threadIdx.x == 0) a.out_ids[(int64_t)b * (n + 1) + t0 + i] = xs[i];
       acc = i + 1;
     }
     t = t0 + acc;
     if (acc < 8) break;
   }
-  if (tid == 0) a.num_accepted[b] = t;
-  for (int k = t + 1 + tid; k <= n; k += kSampThreads) out[k] = -1;
+  return t;
+}
 
-  // ---- the row to draw from: the residual at the rejection (p_t itself if
-  // the residual is all zero), else p_n
-  const float* prow = p_b + (int64_t)t * V;
-  const float* qrow = t < n ? q_b + (int64_t)t * V : nullptr;
-  const int ntiles = (V + kSampThreads - 1) / kSampThreads;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) qrow = nullptr;
-    if (tid == 0) lastpos = -1;
-    __syncthreads();
-    int mylast = -1;
-    for (int t0 = 0; t0 < ntiles; t0 += kSampUnroll) {
-      float w[kSampUnroll];
-      row_weights<kSampUnroll>(prow, qrow, t0 * kSampThreads + tid, V, w);
-#pragma unroll
-      for (int u = 0; u < kSampUnroll; ++u) {
-        if (w[u] > 0.f) mylast = (t0 + u) * kSampThreads + tid;
-        const float sw = wave_sum(w[u]);
-        if (lane == 0) wsum[u][wave] = sw;
-      }
-      __syncthreads();
-      if (tid < kSampUnroll && t0 + tid < ntiles) {   // fixed order over the waves
-        float x = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) x += wsum[tid][w2];
-        tile_sum[t0 + tid] = x;
-      }
-      __syncthreads();
-    }
-    atomicMax(&lastpos, mylast);
-    __syncthreads();
-    if (lastpos < 0 && qrow != nullptr) continue;   // all-zero residual: draw from p_t
-    break;
+// Tile sums: grid (chunks, batch).  ws[b][tile] = (residual sum, plain sum,
+// last positive residual entry, last positive plain entry) of the row the
+// draw reads; the residual fields are 0 / -1 when no draft was rejected.
+__global__ __launch_bounds__(kSumThreads) void spec_tile_sums_kernel(SampleArgs a, float4* ws,
+                                                                     int tiles_per_group) {
+  constexpr int NW = kSumThreads / 64;
+  __shared__ float part[kSumUnroll][2][NW];
+  __shared__ int plast[kSumUnroll][2][NW];
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.num_spec, V = a.vocab;
+  const int t = accept_chain(a, b, chunk == 0);
+  if (chunk == 0) {
+    if (tid == 0) a.num_accepted[b] = t;
+    for (int k = t + 1 + tid; k <= n; k += kSumThreads) a.out_ids[(int64_t)b * (n + 1) + k] = -1;
   }
+  const float* prow = a.target_probs + ((int64_t)b * (n + 1) + t) * V;
+  const bool resid = t < n;
+  const float* qrow = resid ? a.draft_probs + ((int64_t)b * n + t) * V : nullptr;
+  const int ntiles = (V + kTile - 1) / kTile;
+  const int t_begin = chunk * tiles_per_group;
+  const int t_end = min(ntiles, t_begin + tiles_per_group);
+  for (int t0 = t_begin; t0 < t_end; t0 += kSumUnroll) {
+    // all reads first (clamped into the row), then the sums
+    float pv[kSumUnroll][kTile / kSumThreads], qv[kSumUnroll][kTile / kSumThreads];
+    if (resid) {
+#pragma unroll
+      for (int u = 0; u < kSumUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < kTile / kSumThreads; ++j) {
+          const int k = min((t0 + u) * kTile + j * kSumThreads + tid, V - 1);
+          pv[u][j] = prow[k];
+          qv[u][j] = qrow[k];
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSumUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < kTile / kSumThreads; ++j) {
+          pv[u][j] = prow[min((t0 + u) * kTile + j * kSumThreads + tid, V - 1)];
+          qv[u][j] = 0.f;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kSumUnroll; ++u) {
+      float rs = 0.f, ps = 0.f;
+      int rl = -1, pl = -1;
+#pragma unroll
+      for (int j = 0; j < kTile / kSumThreads; ++j) {
+        const int k = (t0 + u) * kTile + j * kSumThreads + tid;
+        const bool in = k < V && t0 + u < t_end;
+        const float p = in ? pv[u][j] : 0.f;
+        const float r = in && resid ? fmaxf(p - qv[u][j], 0.f) : 0.f;
+        rs += r;
+        ps += p;
+        if (r > 0.f) rl = k;
+        if (p > 0.f) pl = k;
+      }
+      rs = wave_sum(rs);
+      ps = wave_sum(ps);
+      rl = wave_max(rl);
+      pl = wave_max(pl);
+      if (lane == 0) {
+        part[u][0][wave] = rs;
+        part[u][1][wave] = ps;
+        plast[u][0][wave] = rl;
+        plast[u][1][wave] = pl;
+      }
+    }
+    __syncthreads();
+    if (tid < kSumUnroll && t0 + tid < t_end) {   // fixed order over the waves
+      float rs = 0.f, ps = 0.f;
+      int rl = -1, pl = -1;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        rs += part[tid][0][w];
+        ps += part[tid][1][w];
+        rl = max(rl, plast[tid][0][w]);
+        pl = max(pl, plast[tid][1][w]);
+      }
+      ws[(int64_t)b * ntiles + t0 + tid] =
+          make_float4(rs, ps, __int_as_float(rl), __int_as_float(pl));
+    }
+    __syncthreads();
+  }
+}
 
-  // ---- wave 0: inclusive prefix over the tiles; the first tile past s * total
+// Draw: one work group per request, after the tile sums.
+__global__ __launch_bounds__(kDrawThreads) void spec_draw_kernel(SampleArgs a, const float4* ws) {
+  __shared__ float tile_sum[kSampMaxTiles];
+  __shared__ float wsum[kDrawThreads / 64];
+  __shared__ int found, tile_last, tile_s, lastpos, use_plain;
+  __shared__ float thr_s, excl_s;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.num_spec, V = a.vocab;
+  const int t = a.num_accepted[b];
+  const int ntiles = (V + kTile - 1) / kTile;
+  const float4* wsb = ws + (int64_t)b * ntiles;
+  // residual unless no draft was rejected or the residual is all zero
+  if (wave == 0) {
+    int last_r = -1;
+    for (int c = lane; c < ntiles; c += 64) last_r = max(last_r, __float_as_int(wsb[c].z));
+    last_r = wave_max(last_r);
+    const int plain = (t >= n || last_r < 0) ? 1 : 0;
+    int last = -1;
+    for (int c = lane; c < ntiles; c += 64)
+      last = max(last, __float_as_int(plain ? wsb[c].w : wsb[c].z));
+    last = wave_max(last);
+    if (lane == 0) {
+      use_plain = plain;
+      lastpos = last;
+    }
+  }
+  __syncthreads();
+  const bool plain = use_plain != 0;
+  const float* prow = a.target_probs + ((int64_t)b * (n + 1) + t) * V;
+  const float* qrow = plain ? nullptr : a.draft_probs + ((int64_t)b * n + t) * V;
+  // wave 0: inclusive prefix over the tiles; the first tile past s * total
   if (wave == 0) {
     float total = 0.f;
     for (int c = 0; c < ntiles; c += 64) {
-      float x = c + lane < ntiles ? tile_sum[c + lane] : 0.f;
+      float x = c + lane < ntiles ? (plain ? wsb[c + lane].y : wsb[c + lane].x) : 0.f;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(x, o);
@@ -176,23 +231,24 @@ __global__ __launch_bounds__(kSampThreads) void spec_sample_kernel(SampleArgs a)
     }
   }
   __syncthreads();
-  // ---- rescan that tile: the first element whose running sum passes s * total
+  // rescan that tile: the first entry whose running sum passes s * total
   const int tile = tile_s;
   if (tile < ntiles) {
-    const int k = tile * kSampThreads + tid;
-    float w1[1];
-    row_weights<1>(prow, qrow, k, V, w1);
-    const float w = w1[0];
+    const int k = tile * kTile + tid;
+    const int kc = min(k, V - 1);
+    float w = prow[kc];
+    if (qrow != nullptr) w = fmaxf(w - qrow[kc], 0.f);
+    if (k >= V) w = 0.f;
     float x = w;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
-    if (lane == 63) wsum[0][wave] = x;
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
     float off = excl_s;
-    for (int w2 = 0; w2 < wave; ++w2) off += wsum[0][w2];
+    for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
     if (w > 0.f) {
       atomicMax(&tile_last, k);
       if (off + x > thr_s) atomicMin(&found, k);
@@ -200,17 +256,32 @@ __global__ __launch_bounds__(kSampThreads) void spec_sample_kernel(SampleArgs a)
     __syncthreads();
   }
   if (tid == 0) {
-    // rounding can leave no element of the tile past the threshold: take its
+    // rounding can leave no entry of the tile past the threshold: take its
     // last positive entry; no tile at all: the row's last positive entry
     int pick = lastpos;
     if (tile < ntiles) pick = found != 0x7fffffff ? found : (tile_last >= 0 ? tile_last : lastpos);
-    out[t] = pick >= 0 ? pick : V - 1;
+    a.out_ids[(int64_t)b * (n + 1) + t] = pick >= 0 ? pick : V - 1;
   }
 }
 
-hipError_t launch_spec_sample(const SampleArgs& a, hipStream_t s) {
+size_t spec_sample_workspace_bytes(int32_t batch, int32_t vocab) {
+  return (size_t)batch * (size_t)((vocab + kTile - 1) / kTile) * sizeof(float4);
+}
+
+hipError_t launch_spec_sample(const SampleArgs& a, void* ws, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(spec_sample_kernel, dim3(a.batch), dim3(kSampThreads), 0, s, a);
+  const int ntiles = (a.vocab + kTile - 1) / kTile;
+  // about 1024 work groups in all, whole groups of kSumUnroll tiles each
+  int groups = (1024 + a.batch - 1) / a.batch;
+  int per = (ntiles + groups - 1) / groups;
+  per = ((per + kSumUnroll - 1) / kSumUnroll) * kSumUnroll;
+  groups = (ntiles + per - 1) / per;
+  hipLaunchKernelGGL(spec_tile_sums_kernel, dim3(groups, a.batch), dim3(kSumThreads), 0, s, a,
+                     static_cast<float4*>(ws), per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_draw_kernel, dim3(a.batch), dim3(kDrawThreads), 0, s, a,
+                     static_cast<const float4*>(ws));
   return hipGetLastError();
 }
 

@@ -240,3 +240,20 @@ def test_custom_mask_refusals_and_plan():
     bad0[0] = -1
     with pytest.raises(pk.PkvError, match="mask_indptr"):
         pk.plan_host(**base, custom_mask=data, mask_indptr=bad0)
+
+
+def test_sampling_refusals_on_host():
+    lib = pk.load_library()
+    assert lib.pkv_chain_speculative_sampling_workspace_size(64, 128256) == 64 * 126 * 16
+    assert lib.pkv_chain_speculative_sampling_workspace_size(0, 10) == 0
+    fake = 1 << 20   # aligned, never dereferenced: every call below is refused on the host
+    call = lambda B, n, V, ws, wsb: lib.pkv_chain_speculative_sampling(
+        fake, fake, fake, fake, fake, B, n, V, fake, fake, ws, wsb, None)
+    assert call(0, 4, 100, None, 0) == 0                               # empty batch
+    assert call(-1, 4, 100, fake, 1 << 20) == pk.PKV_EINVAL
+    assert call(2, -1, 100, fake, 1 << 20) == pk.PKV_EINVAL
+    assert call(2, 4, 0, fake, 1 << 20) == pk.PKV_EINVAL
+    assert call(2, 4, (1 << 20) + 1, fake, 1 << 30) == pk.PKV_EINVAL
+    assert call(2, 4, 5000, fake, 16) == pk.PKV_EWORKSPACE            # 2 x 5 tiles x 16 B needed
+    assert call(2, 4, 5000, None, 1 << 20) == pk.PKV_EWORKSPACE
+    assert call(2, 4, 5000, fake + 4, 1 << 20) == pk.PKV_ELAYOUT
