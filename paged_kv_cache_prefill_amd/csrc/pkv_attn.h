@@ -146,17 +146,42 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     kin[m] = lslot * a.k_s_tok + koff[m];
     vin[m] = lslot * a.v_s_tok + voff[m];
   }
+  // PM 3 on complete tiles (j0 is a multiple of NWG): instruction m covers
+  // tile rows r0 .. r0 + RPI - 1, r0 = (m * NWAVE + wave) * RPI, all on page
+  // table entry (j0 >> shift) + (r0 >> shift) at slots (j0 & pmask) +
+  // (r0 & pmask) + i.  kfull / vfull hold the lane's byte offset from that
+  // page's slot j0 & pmask (which is 0 when pages are not longer than a tile).
+  const uint32_t pmask = (uint32_t)a.page_size - 1;
+  uint32_t kfull[NI], vfull[NI];
+  int32_t pidx[NI];   // page-table entry of instruction m, relative to j0 >> shift
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const uint32_t r0 = (uint32_t)((m * NWAVE + wave) * RPI);
+    const uint32_t sl = (r0 & pmask) + (uint32_t)(lane / CH);
+    kfull[m] = (sl * a.k_s_tok + koff[m]) * (uint32_t)sizeof(T);
+    vfull[m] = (sl * a.v_s_tok + voff[m]) * (uint32_t)sizeof(T);
+    pidx[m] = (int32_t)(r0 >> a.page_shift);
+  }
+  // page strides in bytes: PM 3 is launched only where they fit 32 bits
+  const uint32_t kpage_b = a.k_s_page * (uint32_t)sizeof(T), vpage_b = a.v_s_page * (uint32_t)sizeof(T);
+  const uint32_t ktok_b = a.k_s_tok * (uint32_t)sizeof(T), vtok_b = a.v_s_tok * (uint32_t)sizeof(T);
   // page (and, on the general path, slot) of each lane row of the next tile
   uint32_t lpage[NI], lslot[NI];
   uint32_t spage[NI];       // PM 3: page of each load instruction's rows (scalar)
   const int32_t* ptab = a.pages + rq.page_off;
   const const_i32* ptab_s = (const const_i32*)ptab;   // scalar loads
-  auto fetch_pages = [&](int j0) {
+  auto fetch_pages = [&](int j0) __attribute__((always_inline)) {
     if constexpr (PM == 3) {
+      if (j0 + NWG <= it.kv_end) {
+        const const_i32* pt = ptab_s + (j0 >> a.page_shift);
 #pragma unroll
-      for (int m = 0; m < NI; ++m)
-        spage[m] = (uint32_t)ptab_s[(uint32_t)min(j0 + (m * NWAVE + wave) * RPI, last_key) >>
-                                    a.page_shift];
+        for (int m = 0; m < NI; ++m) spage[m] = (uint32_t)pt[pidx[m]];
+      } else {
+#pragma unroll
+        for (int m = 0; m < NI; ++m)
+          spage[m] = (uint32_t)ptab_s[(uint32_t)min(j0 + (m * NWAVE + wave) * RPI, last_key) >>
+                                      a.page_shift];
+      }
       return;
     }
     if (PM == 1 && j0 + NWG <= it.kv_end) {
@@ -176,56 +201,57 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  auto issue_tile = [&](int j0, uint4* kdst, uint4* vdst) {
+  // Direct loads of the K (is_k) or the V half of tile j0 into dst.
+  auto issue_part = [&](auto is_k, int j0, uint4* dst) __attribute__((always_inline)) {
+    constexpr bool IK = decltype(is_k)::value;
+    const T* pool = IK ? kp : vp;
+    const int full = j0 + NWG <= it.kv_end;
     if constexpr (PM == 3) {
       // one page per instruction: SGPR base + per-lane 32-bit byte offset
-      const char* kb = reinterpret_cast<const char*>(kp);
-      const char* vb = reinterpret_cast<const char*>(vp);
-      const uint32_t lk = (uint32_t)(uintptr_t)kdst, lv = (uint32_t)(uintptr_t)vdst;
-      const uint32_t pmask = (uint32_t)a.page_size - 1;
-      const bool full = j0 + NWG <= it.kv_end;
+      const char* pb = reinterpret_cast<const char*>(pool);
+      const uint32_t ld = (uint32_t)(uintptr_t)dst;
+      const uint32_t page_b = IK ? kpage_b : vpage_b, tok_b = IK ? ktok_b : vtok_b;
+      if (full) {
+        // complete tile: per instruction one 64-bit page base (SGPRs)
+        const char* b0 = pb + ((uint32_t)j0 & pmask) * tok_b;
 #pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        const int rk = j0 + (m * NWAVE + wave) * RPI;
-        const uint32_t lofs = (uint32_t)((m * NWAVE + wave) * 64 * 16);
-        const char* kpg = kb + (uint64_t)spage[m] * a.k_s_page * sizeof(T);
-        const char* vpg = vb + (uint64_t)spage[m] * a.v_s_page * sizeof(T);
-        if (full) {
-          const uint32_t slot0 = (uint32_t)rk & pmask;
-          dma16(kpg + slot0 * a.k_s_tok * sizeof(T), kin[m] * sizeof(T), lk + lofs);
-          dma16(vpg + slot0 * a.v_s_tok * sizeof(T), vin[m] * sizeof(T), lv + lofs);
-        } else {
-          const uint32_t slot = (uint32_t)min(rk + lane / CH, last_key) & pmask;
-          dma16(kpg, (slot * a.k_s_tok + koff[m]) * sizeof(T), lk + lofs);
-          dma16(vpg, (slot * a.v_s_tok + voff[m]) * sizeof(T), lv + lofs);
+        for (int m = 0; m < NI; ++m)
+          dma16(b0 + (uint64_t)spage[m] * page_b, IK ? kfull[m] : vfull[m],
+                ld + (uint32_t)((m * NWAVE + wave) * 64 * 16));
+      } else {
+        // last, partial tile: rows past the end read the last key; the
+        // lane's offset is kfull / vfull moved from slot sl to its clamped slot
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
+          const int r0 = (m * NWAVE + wave) * RPI;
+          const uint32_t slot = (uint32_t)min(j0 + r0 + lane / CH, last_key) & pmask;
+          const uint32_t sl = ((uint32_t)r0 & pmask) + (uint32_t)(lane / CH);
+          dma16(pb + (uint64_t)spage[m] * page_b, (IK ? kfull[m] : vfull[m]) + (slot - sl) * tok_b,
+                ld + (uint32_t)((m * NWAVE + wave) * 64 * 16));
         }
       }
-    } else if (PM == 1 && j0 + NWG <= it.kv_end) {
+    } else if (PM == 1 && full) {
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const uint64_t ko = (uint64_t)lpage[m] * a.k_s_page + kin[m];
-        const uint64_t vo = (uint64_t)lpage[m] * a.v_s_page + vin[m];
-        const int base = (m * NWAVE + wave) * 64;
-        load_lds16(kp + ko, kdst + base);
-        load_lds16(vp + vo, vdst + base);
+        const uint64_t o = (uint64_t)lpage[m] * (IK ? a.k_s_page : a.v_s_page) + (IK ? kin[m] : vin[m]);
+        load_lds16(pool + o, dst + (m * NWAVE + wave) * 64);
       }
     } else {
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
         const KeyLoc l{lpage[m], lslot[m]};
-        const uint64_t ko = key_offset(l, a.k_s_page, a.k_s_tok, koff[m]);
-        const uint64_t vo = key_offset(l, a.v_s_page, a.v_s_tok, voff[m]);
-        const int base = (m * NWAVE + wave) * 64;
-        load_lds16(kp + ko, kdst + base);
-        load_lds16(vp + vo, vdst + base);
+        const uint64_t o = IK ? key_offset(l, a.k_s_page, a.k_s_tok, koff[m])
+                              : key_offset(l, a.v_s_page, a.v_s_tok, voff[m]);
+        load_lds16(pool + o, dst + (m * NWAVE + wave) * 64);
       }
     }
   };
 
-  // One LDS tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](auto masked, const uint4* kt, const char* vt, int j0) {
+  // Scores of the current tile, turned into probabilities P in place.
+  f32x4 s[KB][QB];
+  // S^T = K Q^T, mask, online softmax: s becomes P.
+  auto tile_s = [&](auto masked, const uint4* kt, int j0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    f32x4 s[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -332,7 +358,9 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       }
       l_run[qb] += rs;
     }
+  };
 
+  auto tile_pv = [&](const char* vt) __attribute__((always_inline)) {
     // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
     // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
     // S^T left them.  The A operand (V^T) comes from two transposing LDS
@@ -365,12 +393,16 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
   };
 
-  auto run_tile = [&](const uint4* kt, const uint4* vt, int j0) {
-    const char* vtc = reinterpret_cast<const char*>(vt);
+  auto run_s = [&](const uint4* kt, int j0) __attribute__((always_inline)) {
     if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
-      tile(Flag<false>{}, kt, vtc, j0);
+      tile_s(Flag<false>{}, kt, j0);
     else
-      tile(Flag<true>{}, kt, vtc, j0);
+      tile_s(Flag<true>{}, kt, j0);
+  };
+  // One LDS tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto run_tile = [&](const uint4* kt, const uint4* vt, int j0) __attribute__((always_inline)) {
+    run_s(kt, j0);
+    tile_pv(reinterpret_cast<const char*>(vt));
   };
 
   if constexpr (kFp8) {
@@ -384,7 +416,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     const uint8_t* kb8 = static_cast<const uint8_t*>(a.k);
     const uint8_t* vb8 = static_cast<const uint8_t*>(a.v);
     uint4 kst[M8], vst[M8];
-    auto load8 = [&](int j0) {
+    auto load8 = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < M8; ++m) {
         const int gc = tid + m * 64 * NWAVE;
@@ -397,7 +429,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
             vb8 + key_offset(l, a.v_s_page, a.v_s_tok, (uint32_t)it.kvh * a.v_s_head + c16 * 16));
       }
     };
-    auto store8 = [&](uint4* kdst, uint4* vdst) {
+    auto store8 = [&](uint4* kdst, uint4* vdst) __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < M8; ++m) {
         const int gc = tid + m * 64 * NWAVE;
@@ -428,35 +460,90 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       if (t + 2 < ntiles) store8(lds_k0, lds_v0);
       __syncthreads();
     }
+  } else if constexpr (WN == 1) {
+    // One barrier per tile: K and V of tile t + 1 are issued together as
+    // tile t starts and waited for as it ends.
+    if (ntiles > 0) {
+      fetch_pages(it.tile_begin);
+      issue_part(Flag<true>{}, it.tile_begin, lds_k0);
+      issue_part(Flag<false>{}, it.tile_begin, lds_v0);
+      if (ntiles > 1) fetch_pages(it.tile_begin + NWG);
+    }
+    wait_all();
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      const int j0 = it.tile_begin + t * NWG;
+      // even tile: compute from buffer 0 while buffer 1 fills
+      if (t + 1 < ntiles) {
+        issue_part(Flag<true>{}, j0 + NWG, lds_k1);
+        issue_part(Flag<false>{}, j0 + NWG, lds_v1);
+        if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
+      }
+      run_tile(lds_k0, lds_v0, j0);
+      wait_all();
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      // odd tile: compute from buffer 1 while buffer 0 fills
+      if (t + 2 < ntiles) {
+        issue_part(Flag<true>{}, j0 + 2 * NWG, lds_k0);
+        issue_part(Flag<false>{}, j0 + 2 * NWG, lds_v0);
+        if (t + 3 < ntiles) fetch_pages(j0 + 3 * NWG);
+      }
+      run_tile(lds_k1, lds_v1, j0 + NWG);
+      wait_all();
+      __syncthreads();
+    }
   } else {
+  // Short tiles: direct loads, K and V staggered by half a tile.  Tile t's
+  // keys go to lds_k[t % 2] and its values to lds_v[t % 2]; V(t + 1) is
+  // issued as tile t starts and K(t + 2) once every wave has finished S(t),
+  // so each load has about one and a half tiles of compute to land.  The
+  // per-wave counter waits below rely on these loads completing in issue
+  // order (K0 V0 | K1 | V1 K2 | V2 K3 ...): the wait before S(t + 1) leaves
+  // V(t + 1) and K(t + 2) in flight, the one before PV(t) leaves K(t + 1)
+  // and V(t + 1); the barrier after each wait makes every wave's loads
+  // visible.  Other vector memory accesses issued in between (page-id
+  // loads) only make the waits stricter.  The first wait is a full one: it
+  // also covers the Q loads, which the compiler tracks (it then knows they
+  // are done inside the loop).
+  const int tb = it.tile_begin;
   if (ntiles > 0) {
-    fetch_pages(it.tile_begin);
-    issue_tile(it.tile_begin, lds_k0, lds_v0);
-    if (ntiles > 1) fetch_pages(it.tile_begin + NWG);
+    fetch_pages(tb);
+    issue_part(Flag<true>{}, tb, lds_k0);
+    issue_part(Flag<false>{}, tb, lds_v0);
+    if (ntiles > 1) fetch_pages(tb + NWG);
   }
   wait_all();
   __syncthreads();
+  if (ntiles > 1) issue_part(Flag<true>{}, tb + NWG, lds_k1);
 
-  for (int t = 0; t < ntiles; t += 2) {
-    const int j0 = it.tile_begin + t * NWG;
-    // even tile: compute from buffer 0 while buffer 1 fills
+  // one tile; BUF is t % 2
+  auto step = [&](auto buf, int t) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf)::value;
+    uint4* kc = BUF ? lds_k1 : lds_k0;
+    uint4* vc = BUF ? lds_v1 : lds_v0;
+    uint4* vn = BUF ? lds_v0 : lds_v1;
+    const int j0 = tb + t * NWG;
     if (t + 1 < ntiles) {
-      issue_tile(j0 + NWG, lds_k1, lds_v1);
+      issue_part(Flag<false>{}, j0 + NWG, vn);          // V(t + 1)
       if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
     }
-    run_tile(lds_k0, lds_v0, j0);
-    wait_all();
+    run_s(kc, j0);
+    if (t + 1 < ntiles) wait_vm_lgkm0<2 * NI>(); else wait_vm_lgkm0<0>();   // V(t) landed
     __syncthreads();
-    if (t + 1 >= ntiles) break;
-    // odd tile: compute from buffer 1 while buffer 0 fills
-    if (t + 2 < ntiles) {
-      issue_tile(j0 + 2 * NWG, lds_k0, lds_v0);
-      if (t + 3 < ntiles) fetch_pages(j0 + 3 * NWG);
+    if (t + 2 < ntiles) issue_part(Flag<true>{}, j0 + 2 * NWG, kc);        // K(t + 2)
+    tile_pv(reinterpret_cast<const char*>(vc));
+    if (t + 1 < ntiles) {
+      if (t + 2 < ntiles) wait_vm_lgkm0<2 * NI>(); else wait_vm_lgkm0<NI>();  // K(t + 1) landed
+      __syncthreads();
     }
-    run_tile(lds_k1, lds_v1, j0 + NWG);
-    wait_all();
-    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(Flag<0>{}, t);
+    if (t + 1 >= ntiles) break;
+    step(Flag<1>{}, t + 1);
   }
+  __syncthreads();   // the epilogue below reuses the buffers
   }   // FP8 / direct-load paths
 
   // ---- epilogue
@@ -605,7 +692,12 @@ static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream
   if (a.num_work == 0) return hipSuccess;
   const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
   if constexpr ((VAR & 4) != 0) return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);  // FP8: one path
-  if (pow2 && a.page_size >= 512 / D) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
+  const bool page_b32 = (uint64_t)a.k_s_page * sizeof(T) < (1ull << 32) &&
+                        (uint64_t)a.v_s_page * sizeof(T) < (1ull << 32);
+  if (pow2 && a.page_size >= 512 / D) {
+    if (page_b32) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
+    return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);   // pages of 4 GiB or more
+  }
   if (pow2) return launch_attention_pm<T, D, 1, VAR>(tile_kind, a, s);
   return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);
 }

@@ -134,6 +134,14 @@ __device__ __forceinline__ void e4m3x16_to(uint4 in, uint4& lo, uint4& hi) {
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 // Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait until at most N vector memory loads of this wave are outstanding and
+// every LDS / scalar memory access has completed (gfx9 s_waitcnt encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 // Two transposing 8-byte LDS reads joined into one 8-element fragment.
 __device__ __forceinline__ i16x8 lds_read_tr16_x2(const char* p0, const char* p1) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
