@@ -256,6 +256,11 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The score products run at raised wave priority: the other wave on the
+    // SIMD then fills the gaps with its softmax or PV work instead of
+    // interleaving its own matrix products into this burst, whose results
+    // gate everything after it in this wave.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
 #pragma unroll
@@ -266,6 +271,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(af, qf[qb][dk], s[kb][qb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
     const int jl = j0 + wn * NW + 4 * g;

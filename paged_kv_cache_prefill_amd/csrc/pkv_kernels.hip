@@ -49,40 +49,50 @@ namespace pkv {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   // TPR threads own one row (4 head-dim elements each); a work group covers
-  // RPW rows of one split query tile.  The threads of a row split the slots
-  // for the max and the weight sum (reduced with shuffles inside the row's
-  // TPR-lane group), then every thread sweeps all slots for its 4 elements,
-  // the slot weights broadcast from the thread that computed them; the
-  // partial-o loads of different slots are independent, so they overlap.
+  // RPW rows of one split query tile.  Every thread sweeps the slots for its
+  // 4 elements, U slots per step with all their loads (partial o and lse)
+  // issued together (an index past the last slot re-reads the last one with
+  // weight 0), keeping a running maximum of the slot lse values and
+  // rescaling its sums when a step raises it; at most U slots take one
+  // round trip to memory.
   constexpr int TPR = D / 4;
   constexpr int RPW = 256 / TPR;
+  constexpr int U = 16;
   const MergeItem it = a.items[blockIdx.x];
   const int rl = blockIdx.y * RPW + (int)threadIdx.x / TPR;
   const int d4 = (int)threadIdx.x % TPR;
-  if (rl >= it.nrows) return;                     // whole TPR-lane groups leave together
+  if (rl >= it.nrows) return;
   const ReqInfo rq = a.reqs[it.b];
   const int G = a.group;
   const int64_t tr = a.tile_rows;
   const float* lse = a.part_lse + (int64_t)it.slot0 * tr + rl;   // slot c at lse[c * tr]
   const float* po = a.part_o + ((int64_t)it.slot0 * tr + rl) * D + d4 * 4;
-  float mt = kNegInf;
-  for (int c = d4; c < it.nslots; c += TPR) mt = fmaxf(mt, lse[c * tr]);
-#pragma unroll
-  for (int o = TPR / 2; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, TPR));
-  const float mu = (mt == kNegInf) ? 0.f : mt;
-  float wt = 0.f;
+  float mt = kNegInf, wt = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < it.nslots; c0 += TPR) {
-    const float mw = c0 + d4 < it.nslots ? fast_exp2(lse[(c0 + d4) * tr] - mu) : 0.f;
-    wt += mw;
-    const int cnt = min(TPR, it.nslots - c0);
-    for (int j = 0; j < cnt; ++j) {
-      const float w = __shfl(mw, j, TPR);
-      acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)(c0 + j) * tr * D);
-    }
-  }
+  for (int c0 = 0; c0 < it.nslots; c0 += U) {
+    f32x4 v[U];
+    float l[U];
 #pragma unroll
-  for (int o = TPR / 2; o >= 1; o >>= 1) wt += __shfl_xor(wt, o, TPR);
+    for (int j = 0; j < U; ++j) {
+      const int64_t c = min(c0 + j, it.nslots - 1);
+      l[j] = lse[c * tr];
+      v[j] = *reinterpret_cast<const f32x4*>(po + c * tr * D);
+    }
+    float mn = mt;
+#pragma unroll
+    for (int j = 0; j < U; ++j) mn = fmaxf(mn, l[j]);   // the re-read last slot changes nothing
+    const float mu = (mn == kNegInf) ? 0.f : mn;
+    const float sc = (mt == kNegInf) ? 0.f : fast_exp2(mt - mu);
+    wt *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float w = c0 + j < it.nslots ? fast_exp2(l[j] - mu) : 0.f;
+      wt += w;
+      acc += w * v[j];
+    }
+    mt = mn;
+  }
   const float inv = wt > 0.f ? 1.f / wt : 0.f;
   const int r = it.row0 + rl;
   const int pos = r / G;
