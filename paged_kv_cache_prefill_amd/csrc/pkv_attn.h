@@ -415,55 +415,116 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     // FP8 caches: each thread loads whole 16-byte key-row chunks (16 codes)
     // through the page table into registers while the current tile runs,
     // then converts them into the other LDS buffer (two bf16/fp16 chunks,
-    // same swizzled layout), before the barrier that closes the tile.
+    // same swizzled layout), before the barrier that closes the tile.  The
+    // short-query tiles (one work group per CU, bound by load latency) keep
+    // two tiles of codes in flight in two register sets.
     constexpr int C16 = D / 16;                     // 16-byte FP8 chunks per key row
     constexpr int M8 = NWG * C16 / (64 * NWAVE);    // chunks per thread per tile
+    constexpr int NS = WN > 1 ? 2 : 1;              // register staging sets
     static_assert(M8 >= 1 && NWG * C16 % (64 * NWAVE) == 0, "fp8 tile split");
     const uint8_t* kb8 = static_cast<const uint8_t*>(a.k);
     const uint8_t* vb8 = static_cast<const uint8_t*>(a.v);
-    uint4 kst[M8], vst[M8];
-    auto load8 = [&](int j0) __attribute__((always_inline)) {
+    uint4 kst[NS][M8], vst[NS][M8];
+    // PM 3 (power-of-two pages of at least RPW8 keys): wave instruction m
+    // reads key rows r0 .. r0 + RPW8 - 1 of the tile, r0 = RPW8 * (wave +
+    // NWAVE * m), all on one page, so on complete tiles its page id is a
+    // scalar load and each lane adds a fixed byte offset (its row in the
+    // group and its 16-byte chunk) to a scalar base: the data loads never
+    // wait on per-lane page-id loads, which would hold back (in-order
+    // completion) the loads of the tiles still in flight.
+    constexpr int RPW8 = 64 / C16;
+    const uint32_t f8k = (uint32_t)(lane / C16) * a.k_s_tok + (uint32_t)it.kvh * a.k_s_head +
+                         (uint32_t)(lane % C16) * 16;
+    const uint32_t f8v = (uint32_t)(lane / C16) * a.v_s_tok + (uint32_t)it.kvh * a.v_s_head +
+                         (uint32_t)(lane % C16) * 16;
+    auto load8 = [&](auto set, int j0) __attribute__((always_inline)) {
+      constexpr int S = decltype(set)::value;
+      if (PM == 3 && j0 + NWG <= it.kv_end) {
+        uint32_t pg[M8];   // all page ids first: one wait for the scalar loads
+#pragma unroll
+        for (int m = 0; m < M8; ++m)
+          pg[m] = (uint32_t)ptab_s[(uint32_t)(j0 + RPW8 * (wave + NWAVE * m)) >> a.page_shift];
+#pragma unroll
+        for (int m = 0; m < M8; ++m) {
+          const int r0 = RPW8 * (wave + NWAVE * m);
+          const uint32_t sl = (uint32_t)(j0 + r0) & (uint32_t)(a.page_size - 1);
+          const uint8_t* kr = kb8 + (uint64_t)pg[m] * a.k_s_page + sl * a.k_s_tok;
+          const uint8_t* vr = vb8 + (uint64_t)pg[m] * a.v_s_page + sl * a.v_s_tok;
+          kst[S][m] = *reinterpret_cast<const uint4*>(kr + f8k);
+          vst[S][m] = *reinterpret_cast<const uint4*>(vr + f8v);
+        }
+        // keeps the compiler from sinking these loads towards their use
+        asm volatile("" ::: "memory");
+        return;
+      }
 #pragma unroll
       for (int m = 0; m < M8; ++m) {
         const int gc = tid + m * 64 * NWAVE;
         const int row = gc / C16, c16 = gc - (gc / C16) * C16;
         const KeyLoc l = locate_key(ptab, (uint32_t)min(j0 + row, last_key), a.page_magic,
                                     a.page_shift, (uint32_t)a.page_size);
-        kst[m] = *reinterpret_cast<const uint4*>(
+        kst[S][m] = *reinterpret_cast<const uint4*>(
             kb8 + key_offset(l, a.k_s_page, a.k_s_tok, (uint32_t)it.kvh * a.k_s_head + c16 * 16));
-        vst[m] = *reinterpret_cast<const uint4*>(
+        vst[S][m] = *reinterpret_cast<const uint4*>(
             vb8 + key_offset(l, a.v_s_page, a.v_s_tok, (uint32_t)it.kvh * a.v_s_head + c16 * 16));
       }
     };
-    auto store8 = [&](uint4* kdst, uint4* vdst) __attribute__((always_inline)) {
+    auto store8 = [&](auto set, uint4* kdst, uint4* vdst) __attribute__((always_inline)) {
+      constexpr int S = decltype(set)::value;
 #pragma unroll
       for (int m = 0; m < M8; ++m) {
         const int gc = tid + m * 64 * NWAVE;
         const int row = gc / C16, c = 2 * (gc - (gc / C16) * C16);
         uint4 lo, hi;
-        e4m3x16_to<T>(kst[m], lo, hi);
+        e4m3x16_to<T>(kst[S][m], lo, hi);
         kdst[row * CH + swz_k<CH>(row, c)] = lo;
         kdst[row * CH + swz_k<CH>(row, c + 1)] = hi;
-        e4m3x16_to<T>(vst[m], lo, hi);
+        e4m3x16_to<T>(vst[S][m], lo, hi);
         vdst[row * CH + swz_v<CH>(row, c)] = lo;
         vdst[row * CH + swz_v<CH>(row, c + 1)] = hi;
       }
     };
+    using S0 = Flag<false>;
+    using S1 = Flag<(NS > 1)>;   // the second set, or the first again
+    const int tb = it.tile_begin;
     if (ntiles > 0) {
-      load8(it.tile_begin);
-      store8(lds_k0, lds_v0);
+      load8(S0{}, tb);
+      store8(S0{}, lds_k0, lds_v0);
     }
+    // Q must have landed before the loop: the compiler may issue the Q loads
+    // late, and a wait for them inside the loop would also wait for the
+    // staging loads in flight (in-order completion).
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(qf[qb][dk]));
+    if (NS > 1 && ntiles > 0) load8(S1{}, tb + NWG);
     __syncthreads();
+    // With two sets, raw tile u sits in set u % 2 from two tiles ahead; with
+    // one, tile u + 1 is loaded as tile u starts.  With two sets the loads
+    // and conversions run unconditionally (tiles past the end read the last
+    // key and fill a buffer no one reads): a skipped conversion would leave
+    // the compiler assuming that set's loads may still be pending, and its
+    // waits before reusing the registers would then hold back the loads of
+    // the other set (in-order completion).
     for (int t = 0; t < ntiles; t += 2) {
-      const int j0 = it.tile_begin + t * NWG;
-      if (t + 1 < ntiles) load8(j0 + NWG);
+      const int j0 = tb + t * NWG;
+      if constexpr (NS > 1) {
+        load8(S0{}, j0 + 2 * NWG);
+      } else {
+        if (t + 1 < ntiles) load8(S0{}, j0 + NWG);
+      }
       run_tile(lds_k0, lds_v0, j0);
-      if (t + 1 < ntiles) store8(lds_k1, lds_v1);
+      if (NS > 1 || t + 1 < ntiles) store8(S1{}, lds_k1, lds_v1);
       __syncthreads();
       if (t + 1 >= ntiles) break;
-      if (t + 2 < ntiles) load8(j0 + 2 * NWG);
+      if constexpr (NS > 1) {
+        load8(S1{}, j0 + 3 * NWG);
+      } else {
+        if (t + 2 < ntiles) load8(S0{}, j0 + 2 * NWG);
+      }
       run_tile(lds_k1, lds_v1, j0 + NWG);
-      if (t + 2 < ntiles) store8(lds_k0, lds_v0);
+      if (NS > 1 || t + 2 < ntiles) store8(S0{}, lds_k0, lds_v0);
       __syncthreads();
     }
   } else if constexpr (WN == 1) {
@@ -697,15 +758,21 @@ template <typename T, int D, int VAR>
 static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream_t s) {
   if (a.num_work == 0) return hipSuccess;
   const bool pow2 = (a.page_size & (a.page_size - 1)) == 0;
-  if constexpr ((VAR & 4) != 0) return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);  // FP8: one path
-  const bool page_b32 = (uint64_t)a.k_s_page * sizeof(T) < (1ull << 32) &&
-                        (uint64_t)a.v_s_page * sizeof(T) < (1ull << 32);
-  if (pow2 && a.page_size >= 512 / D) {
-    if (page_b32) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
-    return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);   // pages of 4 GiB or more
+  if constexpr ((VAR & 4) != 0) {
+    // FP8: scalar page ids when a page holds a whole wave instruction's rows
+    if (pow2 && a.page_size >= 64 / (D / 16))
+      return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
+    return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);
+  } else {
+    const bool page_b32 = (uint64_t)a.k_s_page * sizeof(T) < (1ull << 32) &&
+                          (uint64_t)a.v_s_page * sizeof(T) < (1ull << 32);
+    if (pow2 && a.page_size >= 512 / D) {
+      if (page_b32) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
+      return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);   // pages of 4 GiB or more
+    }
+    if (pow2) return launch_attention_pm<T, D, 1, VAR>(tile_kind, a, s);
+    return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);
   }
-  if (pow2) return launch_attention_pm<T, D, 1, VAR>(tile_kind, a, s);
-  return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);
 }
 
 template <int VAR>
