@@ -21,11 +21,12 @@ namespace pkv {
 // fixed on complete tiles), 3 power-of-two pages of at least one load
 // instruction's rows: each instruction stays on one page, so its page id is
 // a scalar load and its address an SGPR base plus a per-lane 32-bit offset,
-// issued from assembly (dma16), which the compiler does not track; the
-// wait-all and barrier closing every tile make those loads visible.  With PM
-// 0 and 1 the last, partial tile of a task takes the general path.  VAR bit
-// 0 adds the custom-mask test on edge tiles, bit 1 the logits soft-cap; each
-// combination is its own instantiation so the plain kernel carries neither.
+// issued from assembly (dma16), which the compiler does not track; explicit
+// counter waits and barriers make those loads visible (see the loops below).
+// With PM 0 and 1 the last, partial tile of a task takes the general path.
+// VAR bit 0 adds the custom-mask test on edge tiles, bit 1 the logits
+// soft-cap, bit 2 FP8 K/V (register-staged, PM 0 or 3); each combination is
+// its own instantiation so the plain kernel carries none of them.
 template <typename T, int D, int WM, int WN, int QB, int NW, int WPE, int PM, int VAR>
 __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   constexpr bool kMask = (VAR & 1) != 0;   // custom topology mask
@@ -134,15 +135,14 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // swz_k / swz_v of it.  Keys at or past kv_end read the last key instead
   // (finite data, masked to zero weight), so no read leaves the request.
   uint32_t koff[NI], voff[NI];   // element offsets of this lane's chunks within a key row
-  uint32_t kin[NI], vin[NI];     // ... plus the lane's fixed slot (PM 1) or row (PM 3)
+  uint32_t kin[NI], vin[NI];     // ... plus the lane's fixed slot on complete tiles (PM 1)
   int lrow[NI];
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
     lrow[m] = (m * NWAVE + wave) * RPI + lane / CH;
     koff[m] = (uint32_t)swz_k<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.k_s_head;
     voff[m] = (uint32_t)swz_v<CH>(lrow[m], lane % CH) * 8 + (uint32_t)it.kvh * a.v_s_head;
-    const uint32_t lslot = PM == 3 ? (uint32_t)(lane / CH)
-                                   : (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
+    const uint32_t lslot = (uint32_t)lrow[m] & (uint32_t)(a.page_size - 1);
     kin[m] = lslot * a.k_s_tok + koff[m];
     vin[m] = lslot * a.v_s_tok + voff[m];
   }

@@ -44,8 +44,12 @@ def _oracle(w, kc, vc):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("page", [1, 3, 16])
+@pytest.mark.parametrize("page", [1, 3, 8, 16, 256])
 def test_fp8_tiny(pk, d, page):
+    # pages 1 and 3 take the per-lane page-table path; power-of-two pages
+    # that hold a whole load instruction's rows (>= 64 / (d / 16) keys: 16,
+    # 8, 4 for d = 64, 128, 256) take the scalar page-id path, 256 with
+    # tiles that start inside a page
     rng = np.random.default_rng(d * 10 + page)
     qo = [1, 23, 70]
     kv = [40, 23, 190]
