@@ -32,6 +32,11 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   constexpr bool kMask = (VAR & 1) != 0;   // custom topology mask
   constexpr bool kCap = (VAR & 2) != 0;    // logits soft-cap
   constexpr bool kFp8 = (VAR & 4) != 0;    // FP8 E4M3 K/V (converted into LDS)
+  // Short tiles on the scalar-page path bring Q in through LDS with the same
+  // untracked direct loads as K and V, so the first key tiles load together
+  // with it (the launcher takes this path only where Q's offsets within a
+  // tile fit 32 bits).
+  constexpr bool kQL = WN > 1 && PM == 3 && !kFp8;
   using Tr = Traits<T>;
   using frag = typename Tr::frag;
   constexpr int NWAVE = WM * WN;
@@ -52,6 +57,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // see that the direct loads into one buffer cannot alias reads of the other
   // (it then keeps those loads in flight across the tile's compute).
   __shared__ uint4 lds_k0[TCH], lds_v0[TCH], lds_k1[TCH], lds_v1[TCH];
+  __shared__ uint4 lds_q[kQL ? MW * WM * (D / 8) : 1];   // Q rows of the task (kQL)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,10 +92,13 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const int pos = r / G;
       mrow[qb] += pos * rq.kv_len;
       const int h = it.kvh * G + (r - pos * G);
-      const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
+      if constexpr (!kQL) {
+        const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
 #pragma unroll
-      for (int dk = 0; dk < DK; ++dk)
-        qf[qb][dk] = __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(src + dk * 32 + g * 8));
+        for (int dk = 0; dk < DK; ++dk)
+          qf[qb][dk] =
+              __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(src + dk * 32 + g * 8));
+      }
       int l0 = 0;
       if (win >= 0) l0 = max(0, pos + shift_q - win);
       const int h0 = a.causal ? pos + shift_q : rq.kv_len - 1;
@@ -574,15 +583,59 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // also covers the Q loads, which the compiler tracks (it then knows they
   // are done inside the loop).
   const int tb = it.tile_begin;
-  if (ntiles > 0) {
-    fetch_pages(tb);
-    issue_part(Flag<true>{}, tb, lds_k0);
-    issue_part(Flag<false>{}, tb, lds_v0);
-    if (ntiles > 1) fetch_pages(tb + NWG);
+  if constexpr (kQL) {
+    // Q rows first (row rr of the task: packed row row0 + rr, rows past the
+    // task re-read its last row), then K0, V0 and K1 before the first wait,
+    // which leaves K1 in flight.  SGPR base: the task's first position; lane
+    // offsets: (position - first) * s_tok + head * s_head + chunk, in bytes.
+    constexpr int QCH = MW * WM * CH;               // 16-byte chunks of the Q rows
+    static_assert(QCH % 64 == 0, "Q rows per wave instruction");
+    const int pos0 = it.row0 / G;
+    const char* qbase = reinterpret_cast<const char*>(qp) +
+                        ((int64_t)(rq.qo_start + pos0) * a.q_s_tok) * (int64_t)sizeof(T);
+    const int rlast = min(it.row0 + it.nrows, R) - 1;
+#pragma unroll
+    for (int i = wave * 64; i < QCH; i += 64 * NWAVE) {
+      const int rr = (i + lane) / CH, c = (i + lane) % CH;
+      const int r = min(it.row0 + rr, rlast);
+      const int pos = r / G;
+      const int h = it.kvh * G + (r - pos * G);
+      const uint32_t off = ((uint32_t)(pos - pos0) * (uint32_t)a.q_s_tok +
+                            (uint32_t)h * (uint32_t)a.q_s_head + (uint32_t)c * 8) *
+                           (uint32_t)sizeof(T);
+      dma16(qbase, off, (uint32_t)(uintptr_t)lds_q + (uint32_t)i * 16);
+    }
+    if (ntiles > 0) {
+      fetch_pages(tb);
+      issue_part(Flag<true>{}, tb, lds_k0);
+      issue_part(Flag<false>{}, tb, lds_v0);
+      if (ntiles > 1) {
+        fetch_pages(tb + NWG);
+        issue_part(Flag<true>{}, tb + NWG, lds_k1);
+      }
+    }
+    if (ntiles > 1) wait_vm_lgkm0<NI>(); else wait_vm_lgkm0<0>();
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int rl = wm * MW + qb * 16 + l16;
+      const bool valid = rl < it.nrows && it.row0 + rl < R;
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk)
+        qf[qb][dk] = valid ? __builtin_bit_cast(frag, lds_q[rl * CH + dk * 4 + g])
+                           : __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0));
+    }
+  } else {
+    if (ntiles > 0) {
+      fetch_pages(tb);
+      issue_part(Flag<true>{}, tb, lds_k0);
+      issue_part(Flag<false>{}, tb, lds_v0);
+      if (ntiles > 1) fetch_pages(tb + NWG);
+    }
+    wait_all();
+    __syncthreads();
+    if (ntiles > 1) issue_part(Flag<true>{}, tb + NWG, lds_k1);
   }
-  wait_all();
-  __syncthreads();
-  if (ntiles > 1) issue_part(Flag<true>{}, tb + NWG, lds_k1);
 
   // one tile; BUF is t % 2
   auto step = [&](auto buf, int t) __attribute__((always_inline)) {
@@ -764,8 +817,13 @@ static hipError_t launch_attention_t(int tile_kind, const AttnArgs& a, hipStream
       return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
     return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);
   } else {
-    const bool page_b32 = (uint64_t)a.k_s_page * sizeof(T) < (1ull << 32) &&
-                          (uint64_t)a.v_s_page * sizeof(T) < (1ull << 32);
+    // 32-bit byte offsets: page strides, and (short tiles, Q through LDS)
+    // a tile's Q rows from its first position
+    const bool page_b32 =
+        (uint64_t)a.k_s_page * sizeof(T) < (1ull << 32) &&
+        (uint64_t)a.v_s_page * sizeof(T) < (1ull << 32) &&
+        ((uint64_t)a.q_s_tok * 33 + (uint64_t)a.q_s_head * a.num_qo_heads + D) * sizeof(T) <
+            (1ull << 32);
     if (pow2 && a.page_size >= 512 / D) {
       if (page_b32) return launch_attention_pm<T, D, 3, VAR>(tile_kind, a, s);
       return launch_attention_pm<T, D, 0, VAR>(tile_kind, a, s);   // pages of 4 GiB or more

@@ -106,9 +106,16 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is listed as clobbered on purpose
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+  // sbase and lds are uniform over the wave; readfirstlane makes that
+  // explicit so the "s" operands get SGPRs even where the compiler's
+  // uniformity analysis cannot prove it (it is free when they already are).
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(lds)
+               : "v"(voff), "s"(reinterpret_cast<const char*>(bs)), "s"(ls)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
