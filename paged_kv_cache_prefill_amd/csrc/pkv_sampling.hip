@@ -103,15 +103,32 @@ __global__ __launch_bounds__(kSumThreads) void spec_tile_sums_kernel(SampleArgs 
   const int ntiles = (V + kTile - 1) / kTile;
   const int t_begin = chunk * tiles_per_group;
   const int t_end = min(ntiles, t_begin + tiles_per_group);
+  // Entry j of tile u for this thread: 4 consecutive entries per thread and
+  // one 16-byte load per row when rows are 16-byte aligned (vocab a multiple
+  // of 4), else entries j * kSumThreads + tid with 4-byte loads.
+  constexpr int E = kTile / kSumThreads;   // entries per thread per tile
+  static_assert(E == 4, "16-byte loads");
+  const bool vec = (V & 3) == 0;
+  auto entry = [&](int tile, int j) { return tile * kTile + (vec ? E * tid + j : j * kSumThreads + tid); };
   for (int t0 = t_begin; t0 < t_end; t0 += kSumUnroll) {
     // all reads first (clamped into the row), then the sums
-    float pv[kSumUnroll][kTile / kSumThreads], qv[kSumUnroll][kTile / kSumThreads];
-    if (resid) {
+    float pv[kSumUnroll][E], qv[kSumUnroll][E];
+    if (vec) {
+#pragma unroll
+      for (int u = 0; u < kSumUnroll; ++u) {
+        const int k4 = min((t0 + u) * kTile + E * tid, V - E);
+        const float4 p4 = *reinterpret_cast<const float4*>(prow + k4);
+        const float4 q4 = resid ? *reinterpret_cast<const float4*>(qrow + k4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        pv[u][0] = p4.x; pv[u][1] = p4.y; pv[u][2] = p4.z; pv[u][3] = p4.w;
+        qv[u][0] = q4.x; qv[u][1] = q4.y; qv[u][2] = q4.z; qv[u][3] = q4.w;
+      }
+    } else if (resid) {
 #pragma unroll
       for (int u = 0; u < kSumUnroll; ++u)
 #pragma unroll
-        for (int j = 0; j < kTile / kSumThreads; ++j) {
-          const int k = min((t0 + u) * kTile + j * kSumThreads + tid, V - 1);
+        for (int j = 0; j < E; ++j) {
+          const int k = min(entry(t0 + u, j), V - 1);
           pv[u][j] = prow[k];
           qv[u][j] = qrow[k];
         }
@@ -119,8 +136,8 @@ __global__ __launch_bounds__(kSumThreads) void spec_tile_sums_kernel(SampleArgs 
 #pragma unroll
       for (int u = 0; u < kSumUnroll; ++u)
 #pragma unroll
-        for (int j = 0; j < kTile / kSumThreads; ++j) {
-          pv[u][j] = prow[min((t0 + u) * kTile + j * kSumThreads + tid, V - 1)];
+        for (int j = 0; j < E; ++j) {
+          pv[u][j] = prow[min(entry(t0 + u, j), V - 1)];
           qv[u][j] = 0.f;
         }
     }
@@ -130,8 +147,8 @@ __global__ __launch_bounds__(kSumThreads) void spec_tile_sums_kernel(SampleArgs 
       float rs = 0.f, ps = 0.f;
       int rl = -1, pl = -1;
 #pragma unroll
-      for (int j = 0; j < kTile / kSumThreads; ++j) {
-        const int k = (t0 + u) * kTile + j * kSumThreads + tid;
+      for (int j = 0; j < E; ++j) {
+        const int k = entry(t0 + u, j);
         const bool in = k < V && t0 + u < t_end;
         const float p = in ? pv[u][j] : 0.f;
         const float r = in && resid ? fmaxf(p - qv[u][j], 0.f) : 0.f;
@@ -169,89 +186,100 @@ __global__ __launch_bounds__(kSumThreads) void spec_tile_sums_kernel(SampleArgs 
   }
 }
 
-// Draw: one work group per request, after the tile sums.
+// Draw: one work group per request, after the tile sums.  Thread c holds
+// tile c's sums (one load per thread, issued with the accepted count), so the
+// choice of row, the prefix over the tiles and the tile to rescan need no
+// further memory round trip; the rescan of that tile is the second.
 __global__ __launch_bounds__(kDrawThreads) void spec_draw_kernel(SampleArgs a, const float4* ws) {
-  __shared__ float tile_sum[kSampMaxTiles];
-  __shared__ float wsum[kDrawThreads / 64];
-  __shared__ int found, tile_last, tile_s, lastpos, use_plain;
-  __shared__ float thr_s, excl_s;
+  constexpr int NWV = kDrawThreads / 64;
+  static_assert(kSampMaxTiles <= kDrawThreads, "one tile per thread");
+  __shared__ float wsum[NWV];
+  __shared__ int wmax_r[NWV], wmax_p[NWV];
+  __shared__ int found, tile_last, first_s;
+  __shared__ float excl_s;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.num_spec, V = a.vocab;
-  const int t = a.num_accepted[b];
   const int ntiles = (V + kTile - 1) / kTile;
-  const float4* wsb = ws + (int64_t)b * ntiles;
-  // residual unless no draft was rejected or the residual is all zero
-  if (wave == 0) {
-    int last_r = -1;
-    for (int c = lane; c < ntiles; c += 64) last_r = max(last_r, __float_as_int(wsb[c].z));
-    last_r = wave_max(last_r);
-    const int plain = (t >= n || last_r < 0) ? 1 : 0;
-    int last = -1;
-    for (int c = lane; c < ntiles; c += 64)
-      last = max(last, __float_as_int(plain ? wsb[c].w : wsb[c].z));
-    last = wave_max(last);
-    if (lane == 0) {
-      use_plain = plain;
-      lastpos = last;
-    }
+  const int t = a.num_accepted[b];
+  float4 e = make_float4(0.f, 0.f, __int_as_float(-1), __int_as_float(-1));
+  if (tid < ntiles) e = ws[(int64_t)b * ntiles + tid];
+  if (tid == 0) {
+    found = 0x7fffffff;
+    tile_last = -1;
+    first_s = ntiles;
+  }
+  // last positive residual / target entry of the row
+  const int lr = wave_max(__float_as_int(e.z)), lp = wave_max(__float_as_int(e.w));
+  if (lane == 0) {
+    wmax_r[wave] = lr;
+    wmax_p[wave] = lp;
   }
   __syncthreads();
-  const bool plain = use_plain != 0;
+  int last_r = -1, last_p = -1;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    last_r = max(last_r, wmax_r[w]);
+    last_p = max(last_p, wmax_p[w]);
+  }
+  // residual unless no draft was rejected or the residual is all zero
+  const bool plain = t >= n || last_r < 0;
+  const int lastpos = plain ? last_p : last_r;
+  // inclusive prefix of the tile sums (wave scans, then the wave totals in
+  // order); the first tile whose prefix passes s * total
+  const float x = tid < ntiles ? (plain ? e.y : e.x) : 0.f;
+  float incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  float off = 0.f, total = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wave) off += wsum[w];
+    total += wsum[w];
+  }
+  incl += off;
+  const float thr = a.sample_u[b] * total;
+  // one LDS atomic per wave (a same-address atomic from every lane would
+  // serialize over the whole work group)
+  {
+    const uint64_t m = __ballot(tid < ntiles && incl > thr);
+    if (lane == 0 && m) atomicMin(&first_s, wave * 64 + __builtin_ctzll(m));
+  }
+  __syncthreads();
+  const int tile = first_s;
+  if (tid == tile) excl_s = incl - x;
+  __syncthreads();
   const float* prow = a.target_probs + ((int64_t)b * (n + 1) + t) * V;
   const float* qrow = plain ? nullptr : a.draft_probs + ((int64_t)b * n + t) * V;
-  // wave 0: inclusive prefix over the tiles; the first tile past s * total
-  if (wave == 0) {
-    float total = 0.f;
-    for (int c = 0; c < ntiles; c += 64) {
-      float x = c + lane < ntiles ? (plain ? wsb[c + lane].y : wsb[c + lane].x) : 0.f;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
-      if (c + lane < ntiles) tile_sum[c + lane] = total + x;
-      total += __shfl(x, 63);
-    }
-    const float thr = a.sample_u[b] * total;
-    int first = ntiles;
-    for (int c = 0; c < ntiles; c += 64) {
-      const uint64_t m = __ballot(c + lane < ntiles && tile_sum[c + lane] > thr);
-      if (m) {
-        first = c + __builtin_ctzll(m);
-        break;
-      }
-    }
-    if (lane == 0) {
-      thr_s = thr;
-      tile_s = first;
-      excl_s = (first > 0 && first < ntiles) ? tile_sum[first - 1] : 0.f;
-      found = 0x7fffffff;
-      tile_last = -1;
-    }
-  }
-  __syncthreads();
   // rescan that tile: the first entry whose running sum passes s * total
-  const int tile = tile_s;
   if (tile < ntiles) {
     const int k = tile * kTile + tid;
     const int kc = min(k, V - 1);
     float w = prow[kc];
     if (qrow != nullptr) w = fmaxf(w - qrow[kc], 0.f);
     if (k >= V) w = 0.f;
-    float x = w;
+    float xs = w;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+      const float y = __shfl_up(xs, o);
+      if (lane >= o) xs += y;
     }
-    if (lane == 63) wsum[wave] = x;
+    __syncthreads();   // every thread has read wsum above
+    if (lane == 63) wsum[wave] = xs;
     __syncthreads();
-    float off = excl_s;
-    for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
-    if (w > 0.f) {
-      atomicMax(&tile_last, k);
-      if (off + x > thr_s) atomicMin(&found, k);
+    float off2 = excl_s;
+    for (int w2 = 0; w2 < wave; ++w2) off2 += wsum[w2];
+    const uint64_t pos = __ballot(w > 0.f);
+    const uint64_t past = __ballot(w > 0.f && off2 + xs > thr);
+    if (lane == 0) {
+      const int kw = tile * kTile + wave * 64;
+      if (pos) atomicMax(&tile_last, kw + 63 - __builtin_clzll(pos));
+      if (past) atomicMin(&found, kw + __builtin_ctzll(past));
     }
     __syncthreads();
   }
