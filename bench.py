@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-coverage]
 
-One step = plan (host validation + scheduling + one async copy) and run
+One step = plan (host validation + scheduling + the task-list upload) and run
 (attention + split merge) over the paged batch-prefill workload: batch 8,
 qo ~ U[128, 1024], kv = qo + U[0, 2048], page 16 in a permuted pool 1.5x the
 pages needed, Hq 32 / Hkv 8, head_dim 128, bf16, causal.  Inputs are resident
@@ -15,7 +15,8 @@ duration comes from HIP events around each launch on the stream it runs on.
 non-causal windows at page 1024 and 16, speculative verify at every batch and
 kv-head count, long-context split-KV with merge) against its roofline.
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
-workload (rank 0, N = 1 only).
+workload (rank 0, N = 1 only).  `copy_ceiling` is the attainable HBM rate of
+a plain device-to-device copy of 1 GiB (read + write bytes over its time).
 """
 from __future__ import annotations
 
@@ -133,6 +134,26 @@ def time_kernel(pk, p, tensors, iters):
         b.record(s)
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def copy_ceiling(torch, dev, nbytes=1 << 30, iters=10):
+    """HBM GB/s of a device-to-device copy (bytes read + bytes written)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(iters):
+        dst.copy_(src)
+    b.record(s)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / ms / 1e6
+    return {"GB/s": gbs, "frac": gbs / PEAK_HBM_GBS, "bytes": 2 * nbytes}
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -463,6 +484,7 @@ def main():
     }
     if not args.no_coverage:
         result["coverage"] = coverage(pk, torch, dev)
+        result["copy_ceiling"] = copy_ceiling(torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result))
