@@ -78,7 +78,10 @@ typedef struct {
   /* 0: automatic; 1: prefill tile (128 packed rows x 64 keys);
      2: short-query tile (16 or 32 packed rows x 128 keys). */
   int32_t tile;
-  int32_t reserved[4];
+  /* > 0: split every task's key range into chunks of this many key tiles
+     (partials merged by run), instead of the automatic choice; 0: automatic. */
+  int32_t split_tiles;
+  int32_t reserved[3];
   /* Topology mask for tree-draft verification (PR #362, Architecture /
      design notes: a causal mask verifies chain drafts only, tree drafts need
      a custom mask).  Host arrays, or NULL for none.  Request b's mask is the

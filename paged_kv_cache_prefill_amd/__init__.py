@@ -52,7 +52,7 @@ class PkvError(ValueError):
 class _PlanOptions(ctypes.Structure):
     _fields_ = [("num_kv_chunks", ctypes.c_int32), ("kv_begin", ctypes.c_int32),
                 ("kv_end", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4),
+                ("split_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
                 ("custom_mask", ctypes.c_void_p), ("mask_indptr", ctypes.c_void_p),
                 ("logits_soft_cap", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
@@ -168,10 +168,12 @@ def _ptr_i32(a):
 
 
 def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0, custom_mask=None,
-             mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None, k_scale=1.0, v_scale=1.0):
+             mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None, k_scale=1.0, v_scale=1.0,
+             split_tiles=0):
     o = _PlanOptions()
     o.num_kv_chunks, o.kv_begin, o.kv_end, o.tile = int(num_kv_chunks), int(kv_begin), \
         int(kv_end), int(tile)
+    o.split_tiles = int(split_tiles)
     o.logits_soft_cap = float(logits_soft_cap or 0.0)
     if kv_dtype is not None:
         if kv_dtype not in ("fp8_e4m3", PKV_FP8_E4M3) and str(kv_dtype) != "torch.float8_e4m3fn":
@@ -389,12 +391,13 @@ def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, 
          head_dim, page_size, causal, window_left=-1, sm_scale=None, dtype="bf16",
          device="cuda", stream=None, num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
          custom_mask=None, mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None, k_scale=1.0,
-         v_scale=1.0):
+         v_scale=1.0, split_tiles=0):
     """Validate and schedule a batch; returns a runnable Plan.
 
     Host int arrays: qo_indptr[B+1], kv_indptr[B+1], kv_page_indices[kv_indptr[B]],
     kv_last_page_len[B].  sm_scale defaults to 1/sqrt(head_dim).
-    num_kv_chunks / kv_begin / kv_end / tile: optional scheduling knobs (see include/pkv.h).
+    num_kv_chunks / kv_begin / kv_end / tile / split_tiles: optional scheduling knobs (see
+    include/pkv.h).
     custom_mask (packed uint8 bits) / mask_indptr (int64 byte offsets [B+1]): a
     per-request topology mask for tree drafts, with causal=False (see include/pkv.h).
     logits_soft_cap > 0 caps every scaled logit s to cap * tanh(s / cap).
@@ -407,14 +410,14 @@ def plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads, 
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
                            tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr,
                            logits_soft_cap=logits_soft_cap, kv_dtype=kv_dtype, k_scale=k_scale,
-                           v_scale=v_scale))
+                           v_scale=v_scale, split_tiles=split_tiles))
 
 
 def plan_host(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
               num_kv_heads, head_dim, page_size, causal, window_left=-1, sm_scale=None,
               dtype="bf16", num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0,
               custom_mask=None, mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None,
-              k_scale=1.0, v_scale=1.0):
+              k_scale=1.0, v_scale=1.0, split_tiles=0):
     """Validate and schedule without a device: an inspectable, non-runnable Plan."""
     return _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
                       num_kv_heads, head_dim, page_size, causal, window_left, sm_scale, dtype,
@@ -422,7 +425,7 @@ def plan_host(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_he
                       dict(num_kv_chunks=num_kv_chunks, kv_begin=kv_begin, kv_end=kv_end,
                            tile=tile, custom_mask=custom_mask, mask_indptr=mask_indptr,
                            logits_soft_cap=logits_soft_cap, kv_dtype=kv_dtype, k_scale=k_scale,
-                           v_scale=v_scale))
+                           v_scale=v_scale, split_tiles=split_tiles))
 
 
 def verify_plan(kv_indptr, kv_page_indices, kv_last_page_len, q_len_per_req, num_qo_heads,

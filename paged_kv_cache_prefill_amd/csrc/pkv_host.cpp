@@ -29,6 +29,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <functional>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -133,6 +134,72 @@ pkv_status check_custom_mask(const pkv_plan_options& o, int32_t batch, int32_t c
   }
   S->mask_bytes = (size_t)total;
   return PKV_OK;
+}
+
+// Chunk size (key tiles) for the automatic split of a launch with few tasks:
+// the candidate whose longest-first schedule over `slots` concurrent work
+// groups ends first, each work item costing its key tiles plus kItemTiles
+// (its start-up latency and, when split, its share of the merge; fitted on
+// the short-query verify batches), if it beats the even-share size
+// `fallback` by 10%.  0 = no split.
+constexpr int64_t kItemTiles = 4;
+int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, int64_t min_tiles,
+                           int64_t fallback) {
+  int64_t longest = 0;
+  for (int64_t c : pieces) longest = std::max(longest, c);
+  std::vector<int64_t> heap;   // slot loads, a min-heap
+  std::vector<int64_t> count;  // remainders by length (counting sort)
+  heap.reserve((size_t)slots);
+  auto makespan = [&](int64_t c) {
+    // full chunks first (all the same size: dealt out evenly), then the
+    // shorter remainders, longest first, each to the least loaded slot
+    const int64_t len = c > 0 ? c : longest;
+    count.assign((size_t)len + 1, 0);
+    int64_t full = 0;
+    for (int64_t n : pieces) {
+      if (n <= 0) continue;
+      if (c > 0) {
+        full += n / c;
+        ++count[(size_t)(n % c)];
+      } else {
+        ++count[(size_t)n];
+      }
+    }
+    const int64_t per = c + kItemTiles, base = full / slots, extra = full % slots;
+    heap.clear();
+    for (int64_t i = 0; i < slots; ++i) heap.push_back((base + (i < extra ? 1 : 0)) * per);
+    int64_t m = (base + (extra > 0 ? 1 : 0)) * per;
+    std::make_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+    for (int64_t r = len; r >= 1; --r) {
+      for (int64_t k = 0; k < count[(size_t)r]; ++k) {
+        std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+        heap.back() += r + kItemTiles;
+        m = std::max(m, heap.back());
+        std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+      }
+    }
+    return m;
+  };
+  int64_t total = 0;
+  for (int64_t n : pieces) total += std::max<int64_t>(n, 0);
+  // the even-share chunk size is kept unless the model expects a schedule at
+  // least 10% shorter (its estimates are only that good)
+  const int64_t fallback_m = makespan(fallback);
+  int64_t best = 0, best_m = makespan(0);
+  for (int64_t c : {4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128}) {
+    if (c < min_tiles || c >= longest) continue;
+    int64_t items = 0;   // far more items than slots never wins: skip those
+    for (int64_t n : pieces) items += (n + c - 1) / c;
+    if (items > 4 * slots) continue;
+    // no schedule beats the average load: skip candidates that cannot win
+    if ((total + items * kItemTiles + slots - 1) / slots >= best_m) continue;
+    const int64_t m = makespan(c);
+    if (m < best_m) {
+      best = c;
+      best_m = m;
+    }
+  }
+  return best_m * 10 <= fallback_m * 9 ? best : fallback;
 }
 
 struct RowTask {
@@ -252,6 +319,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     return fail(PKV_EINVAL, "opts.kv_end: expected >= kv_begin=%d or < 0, given %d", o.kv_begin,
                 o.kv_end);
   if (o.tile < 0 || o.tile > 2) return fail(PKV_EINVAL, "opts.tile: expected 0, 1 or 2, given %d", o.tile);
+  if (o.split_tiles < 0)
+    return fail(PKV_EINVAL, "opts.split_tiles: expected >= 0, given %d", o.split_tiles);
   if (!(o.logits_soft_cap >= 0.f) || !std::isfinite(o.logits_soft_cap))
     return fail(PKV_EINVAL, "opts.logits_soft_cap: expected a finite value >= 0, given %g",
                 (double)o.logits_soft_cap);
@@ -387,28 +456,42 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   }
 
   // ---- split decision: fixed chunk boundaries when asked for, and when the
-  // launch would have fewer than kTargetTasks work groups, chunks longer than
-  // the average share are split further (partials are merged either way)
+  // launch would have fewer than kTargetTasks work groups, the ranges are cut
+  // into chunks of the size choose_chunk_tiles picks (partials are merged
+  // either way)
   auto cost = [&](const RowTask& t) -> int64_t {
     return t.key_lo > t.key_hi ? 0 : (t.key_hi + 1 - t.tile_begin + NK - 1) / NK;
   };
   int64_t chunk_tiles = 0;  // 0: no automatic split
   {
-    int64_t n = 0, total = 0;
+    // pieces: the requested chunks each task's range meets, else the tasks
+    std::vector<int64_t> pieces;
+    pieces.reserve(tasks.size());
     for (const RowTask& t : tasks) {
-      total += cost(t);
-      if (o.num_kv_chunks > 0 && t.key_lo <= t.key_hi) {   // requested chunks the range meets
+      if (o.num_kv_chunks > 0 && t.key_lo <= t.key_hi) {
         const int64_t L = S->reqs[t.b].kv_len;
         int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
         clen = std::max<int64_t>(NK, (clen + NK - 1) / NK * NK);
-        n += t.key_hi / clen - t.key_lo / clen + 1;
+        for (int64_t c0 = t.key_lo / clen * clen; c0 <= t.key_hi; c0 += clen) {
+          const int64_t a = std::max<int64_t>(c0, t.key_lo);
+          const int64_t e = std::min<int64_t>(c0 + clen, (int64_t)t.key_hi + 1);
+          pieces.push_back(e > a ? (e - 1) / NK - a / NK + 1 : 0);
+        }
       } else {
-        n += 1;
+        pieces.push_back(cost(t));
       }
     }
-    if (n < kTargetTasks) {
+    if (o.split_tiles > 0) {
+      chunk_tiles = o.split_tiles;
+    } else if ((int64_t)pieces.size() < kTargetTasks) {
+      // concurrent work groups: two per CU for the 128-row tile at head_dim
+      // <= 128 (64 KB of LDS, two waves per SIMD), one otherwise
+      const int64_t per_cu = (kind == TILE_PREFILL && head_dim <= 128) ? 2 : 1;
       const int64_t min_tiles = (kind == TILE_PREFILL) ? 8 : 4;
-      chunk_tiles = std::max<int64_t>(min_tiles, (total + kTargetTasks - 1) / kTargetTasks);
+      int64_t total = 0;
+      for (int64_t n : pieces) total += n;
+      const int64_t even = std::max<int64_t>(min_tiles, (total + kTargetTasks - 1) / kTargetTasks);
+      chunk_tiles = choose_chunk_tiles(pieces, per_cu * kNumCUs, min_tiles, even);
     }
   }
   std::vector<WorkItem> items;

@@ -69,6 +69,7 @@ def test_plan_refusals():
     refused("EINVAL", kv_last_page_len=[5])
     refused("EINVAL", tile=3)
     refused("EINVAL", num_kv_chunks=-1)
+    refused("EINVAL", split_tiles=-1)
     refused("EINVAL", kv_begin=10, kv_end=5)
 
 
@@ -153,8 +154,39 @@ def test_schedule_covers_every_visible_key(cfg):
                     w.window_left, w.dtype, seed=1, values=False)
     check_coverage(w)
     for opts in ({"num_kv_chunks": 3}, {"tile": 1}, {"tile": 2}, {"kv_begin": 33, "kv_end": 700},
-                 {"num_kv_chunks": 8, "tile": 2}):
+                 {"num_kv_chunks": 8, "tile": 2}, {"split_tiles": 1}, {"split_tiles": 5},
+                 {"num_kv_chunks": 3, "split_tiles": 2}):
         check_coverage(w, **opts)
+
+
+@pytest.mark.parametrize("batch,hkv", [(4, 4), (4, 8), (16, 4), (16, 8), (64, 4), (64, 8)])
+def test_split_choice(batch, hkv):
+    """Forced chunk sizes give items of at most that many key tiles; the
+    automatic choice splits only when tasks are fewer than two per CU, and its
+    chunks are never shorter than four key tiles (the short-query tile)."""
+    w = W.config4(batch=batch, num_kv_heads=hkv, values=False)
+    tasks = batch * hkv
+    for st in (3, 8):
+        p = pk.plan_host(**w.plan_args(), split_tiles=st)
+        it = p.work_items()
+        nk = p.info["tile_keys"]
+        ntiles = (it[:, 5] - it[:, 7] + nk - 1) // nk
+        assert ntiles.max() <= st
+    p = pk.plan_host(**w.plan_args())
+    it = p.work_items()
+    nk = p.info["tile_keys"]
+    if tasks >= 512:
+        assert len(it) == tasks and p.info["num_merge_items"] == 0
+    else:
+        split = it[it[:, 6] >= 0]
+        # every split chunk but a task's last starts on a multiple of the chunk size
+        per_task = {}
+        for row in split:
+            per_task.setdefault((row[0], row[1], row[2]), []).append(row)
+        for rows in per_task.values():
+            rows = sorted(rows, key=lambda r: r[4])
+            for r in rows[:-1]:
+                assert (r[5] - r[7] + nk - 1) // nk >= 4
 
 
 def test_wide_window_schedules_like_no_window():
