@@ -43,6 +43,7 @@ METRIC = "masked-attention TFLOP/s (prefill) + KV HBM GB/s (verify), fraction of
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_prefill_amd", "csrc", f)
                   for f in ("pkv_attn.h", "pkv_device.h", "pkv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_paged_b8_hbm.txt")
+VERIFY_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_verify_b64_hkv8_hbm.txt")
 
 
 def kernel_source_sha():
@@ -53,20 +54,22 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the prefill attention kernel, from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy-kernel
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch of an attention kernel, from a committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy-kernel
     calibration), or None when absent or taken on a different kernel source."""
     try:
         rec = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     rec[k.strip()] = v.strip()
         if rec.get("kernel_source_sha256") != kernel_source_sha():
             return None
-        return float(rec["traffic_bytes_per_launch"])
+        if "traffic_bytes_per_launch" in rec:
+            return float(rec["traffic_bytes_per_launch"])
+        return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -419,6 +422,9 @@ def main():
     ap.add_argument("--kernel-iters", type=int, default=50)
     ap.add_argument("--profile", action="store_true",
                     help="short run for profilers: 3 steps, 1 warmup, no baselines")
+    ap.add_argument("--profile-verify", action="store_true",
+                    help="short run for profilers of the verify workload instead (batch 64, "
+                         "Hkv 8): 5 launches, one JSON line with its algorithmic bytes")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB read + 256 MiB write elementwise kernel "
                          "(scale for the HBM byte counters)")
@@ -443,6 +449,15 @@ def main():
         torch.mul(src, 2.0, out=dst)       # 256 MiB read, 256 MiB written
         torch.cuda.synchronize()
         del src, dst
+
+    if args.profile_verify:
+        w = W.config4(batch=64, num_kv_heads=8, values=False)
+        q, pools = _random_pools(w, dev, 1, seed=7064)
+        p = pk.plan(**w.plan_args(), dtype=torch.bfloat16, device=dev)
+        ms, _ = time_rotating(p, q, pools, 5, warmup=1)
+        print(json.dumps({"workload": "verify_b64_hkv8",
+                          "kv_bytes_per_launch": kv_bytes(w), "eager_ms": ms}))
+        return
 
     w = W.config2(window_left=args.window_left)
     tensors = _device_inputs(w, dev)
@@ -485,6 +500,13 @@ def main():
     if not args.no_coverage:
         result["coverage"] = coverage(pk, torch, dev)
         result["copy_ceiling"] = copy_ceiling(torch, dev)
+        # the short-query verify kernel against the HBM roofline (its largest batch)
+        v = next(r for r in result["coverage"] if r["workload"] == "verify_b64_hkv8")
+        result["roofline_verify"] = {
+            "bound": "hbm", "achieved": v["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": v["GB/s"] / PEAK_HBM_GBS, "traffic": measured_traffic(VERIFY_TRAFFIC_FILE),
+            "kernel": "attn_kernel (short-query tile)", "workload": "verify_b64_hkv8",
+            "kernel_ms": v["ms"]}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result))
