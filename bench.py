@@ -122,21 +122,24 @@ def _device_inputs(w, dev):
     return conv(w.q), conv(w.k_pool), conv(w.v_pool)
 
 
-def time_kernel(pk, p, tensors, iters):
-    """Average run() duration from HIP events on the launch stream (ms)."""
+def time_kernel(pk, p, tensors, iters, warmup=3):
+    """Average run() duration (ms): one pair of HIP events on the launch stream
+    around `iters` back-to-back runs (the host enqueues far faster than the
+    kernel runs, so the stream never waits for it)."""
     import torch
     s = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
     q, k, v = tensors
     o = torch.empty((p.total_q_rows, p.num_qo_heads, p.head_dim), dtype=p.dtype, device=q.device)
     lse = torch.empty((p.total_q_rows, p.num_qo_heads), dtype=torch.float32, device=q.device)
-    for a, b in evs:
-        a.record(s)
+    for _ in range(warmup):
         p.run(q, k, v, out=o, lse=lse)
-        b.record(s)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(iters):
+        p.run(q, k, v, out=o, lse=lse)
+    b.record(s)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return a.elapsed_time(b) / iters
 
 
 def copy_ceiling(torch, dev, nbytes=1 << 30, iters=10):

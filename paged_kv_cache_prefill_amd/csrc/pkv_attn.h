@@ -49,6 +49,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   constexpr int DK = D / 32;            // MFMA k-steps over head_dim
   constexpr int KB = NW / 16;           // 16-key blocks per wave
   constexpr int DB = D / 16;            // 16-wide head_dim blocks of the output
+  constexpr int kReadAhead = 3;         // LDS fragment reads in flight ahead of the products
   static_assert(TCH % (64 * NWAVE) == 0, "tile not divisible among waves");
   static_assert(NW % 32 == 0 && CH >= 8, "shape");
 
@@ -269,18 +270,31 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     // SIMD then fills the gaps with its softmax or PV work instead of
     // interleaving its own matrix products into this burst, whose results
     // gate everything after it in this wave.
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+    {
+      // K fragments are read kReadAhead products ahead of use; the scheduling
+      // barriers (only scalar and vector ALU work may cross them) keep the
+      // compiler from sinking the reads next to their products, where each
+      // would wait out the LDS latency.
+      constexpr int NF = DK * KB, PFK = kReadAhead < NF ? kReadAhead : NF;
+      frag kf[NF];
+      auto ldk = [&](int f) __attribute__((always_inline)) {
+        const int dk = f / KB, kb = f % KB;
         const int row = wn * NW + kb * 16 + l16;
-        const frag af = __builtin_bit_cast(frag, kt[row * CH + swz_k<CH>(row, dk * 4 + g)]);
+        kf[f] = __builtin_bit_cast(frag, kt[row * CH + swz_k<CH>(row, dk * 4 + g)]);
+      };
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(af, qf[qb][dk], s[kb][qb]);
+      for (int f = 0; f < PFK; ++f) ldk(f);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + PFK < NF) ldk(f + PFK);
+        const int dk = f / KB, kb = f % KB;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(kf[f], qf[qb][dk], s[kb][qb]);
+        __builtin_amdgcn_sched_barrier(0x6);   // SALU and VALU may cross
       }
+      __builtin_amdgcn_s_setprio(0);
     }
-    __builtin_amdgcn_s_setprio(0);
 
     // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
     const int jl = j0 + wn * NW + 4 * g;
@@ -382,29 +396,39 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     // reads: lane r of each 16-lane group points at 4 head-dim elements
     // d0 + 4(r%4) of key 4g + r/4 (+16); the read hands lane t element
     // V[4g + k][d0 + t] as its element k.
+    // V^T fragments read kReadAhead products ahead, as the K fragments above
+    constexpr int NS = NW / 32, NF = NS * DB, PFV = kReadAhead < NF ? kReadAhead : NF;
+    frag vf[NF];
+    auto ldv = [&](int f) __attribute__((always_inline)) {
+      const int st = f / DB, db = f % DB;
+      const int key0 = wn * NW + st * 32 + 4 * g + (l16 >> 2);
+      const int key1 = key0 + 16;
+      const int d = db * 16 + 4 * (l16 & 3);        // first of 4 elements this lane points at
+      const int c = d >> 3, off = (d & 7) * 2;      // chunk and byte offset inside it
+      const int a0 = (key0 * CH + swz_v<CH>(key0, c)) * 16 + off;
+      const int a1 = (key1 * CH + swz_v<CH>(key1, c)) * 16 + off;
+      vf[f] = __builtin_bit_cast(frag, lds_read_tr16_x2(vt + a0, vt + a1));
+    };
 #pragma unroll
-    for (int st = 0; st < NW / 32; ++st) {
-      frag pb[QB];
+    for (int f = 0; f < PFV; ++f) ldv(f);
+    frag pb[NS][QB];
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[qb][i] = from_f32<T>(s[2 * st][qb][i]);
-          pb[qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
+          pb[st][qb][i] = from_f32<T>(s[2 * st][qb][i]);
+          pb[st][qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
         }
       }
-      const int key0 = wn * NW + st * 32 + 4 * g + (l16 >> 2);
-      const int key1 = key0 + 16;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 16 + 4 * (l16 & 3);        // first of 4 elements this lane points at
-        const int c = d >> 3, off = (d & 7) * 2;      // chunk and byte offset inside it
-        const int a0 = (key0 * CH + swz_v<CH>(key0, c)) * 16 + off;
-        const int a1 = (key1 * CH + swz_v<CH>(key1, c)) * 16 + off;
-        const frag af = __builtin_bit_cast(frag, lds_read_tr16_x2(vt + a0, vt + a1));
+    for (int f = 0; f < NF; ++f) {
+      if (f + PFV < NF) ldv(f + PFV);
+      const int st = f / DB, db = f % DB;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(af, pb[qb], oacc[db][qb]);
-      }
+      for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = Tr::mfma(vf[f], pb[st][qb], oacc[db][qb]);
+      __builtin_amdgcn_sched_barrier(0x6);   // SALU and VALU may cross
     }
   };
 
