@@ -266,10 +266,11 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The score products run at raised wave priority: the other wave on the
-    // SIMD then fills the gaps with its softmax or PV work instead of
-    // interleaving its own matrix products into this burst, whose results
-    // gate everything after it in this wave.
+    // The score products and the softmax run at raised wave priority (back
+    // to normal as the PV products start): the other wave on the SIMD then
+    // fills the gaps with its PV work instead of interleaving its own matrix
+    // products into this chain, whose results gate everything after it in
+    // this wave.
     {
       // K fragments are read kReadAhead products ahead of use; the scheduling
       // barriers (only scalar and vector ALU work may cross them) keep the
@@ -293,7 +294,6 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Tr::mfma(kf[f], qf[qb][dk], s[kb][qb]);
         __builtin_amdgcn_sched_barrier(0x6);   // SALU and VALU may cross
       }
-      __builtin_amdgcn_s_setprio(0);
     }
 
     // lane owns row l16 of each qb block and keys kb*16 + 4g + i of the slice
@@ -390,6 +390,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   };
 
   auto tile_pv = [&](const char* vt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);   // raised by tile_s
     // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
     // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
     // S^T left them.  The A operand (V^T) comes from two transposing LDS
