@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   constexpr int DK = D / 32;            // MFMA k-steps over head_dim
   constexpr int KB = NW / 16;           // 16-key blocks per wave
   constexpr int DB = D / 16;            // 16-wide head_dim blocks of the output
-  constexpr int kReadAhead = 3;         // LDS fragment reads in flight ahead of the products
+  constexpr int kReadAhead = 4;         // LDS fragment reads in flight ahead of the products
   static_assert(TCH % (64 * NWAVE) == 0, "tile not divisible among waves");
   static_assert(NW % 32 == 0 && CH >= 8, "shape");
 
