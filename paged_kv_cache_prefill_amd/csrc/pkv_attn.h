@@ -390,7 +390,6 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   };
 
   auto tile_pv = [&](const char* vt) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(0);   // raised by tile_s
     // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
     // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
     // S^T left them.  The A operand (V^T) comes from two transposing LDS
@@ -423,6 +422,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           pb[st][qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
         }
       }
+    __builtin_amdgcn_s_setprio(0);   // raised by tile_s, kept over the conversion of P
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if (f + PFV < NF) ldv(f + PFV);
