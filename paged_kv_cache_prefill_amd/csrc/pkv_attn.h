@@ -574,6 +574,24 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
     wait_all();
     __syncthreads();
+    if (wm * MW >= it.nrows || it.row0 + wm * MW >= R) {
+      // a wave holding only padding rows of the task's last row tile: it
+      // issues its share of the loads and meets every barrier of the loop
+      // below (one per tile), computes nothing, and has no row to write
+      for (int t = 0; t + 1 < ntiles; ++t) {
+        const int j0 = it.tile_begin + t * NWG;
+        issue_part(Flag<true>{}, j0 + NWG, (t & 1) ? lds_k0 : lds_k1);
+        issue_part(Flag<false>{}, j0 + NWG, (t & 1) ? lds_v0 : lds_v1);
+        if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
+        wait_all();
+        __syncthreads();
+      }
+      if (ntiles > 0) {
+        wait_all();
+        __syncthreads();
+      }
+      return;
+    }
     for (int t = 0; t < ntiles; t += 2) {
       const int j0 = it.tile_begin + t * NWG;
       // even tile: compute from buffer 0 while buffer 1 fills
