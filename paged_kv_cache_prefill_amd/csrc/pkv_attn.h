@@ -389,7 +389,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
   };
 
-  auto tile_pv = [&](const char* vt) __attribute__((always_inline)) {
+  auto tile_pv_hook = [&](const char* vt, auto&& hook) __attribute__((always_inline)) {
     // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
     // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
     // S^T left them.  The A operand (V^T) comes from two transposing LDS
@@ -422,6 +422,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           pb[st][qb][4 + i] = from_f32<T>(s[2 * st + 1][qb][i]);
         }
       }
+    hook();   // runs once the first V^T reads and the conversion of P are issued
     __builtin_amdgcn_s_setprio(0);   // raised by tile_s, kept over the conversion of P
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -432,6 +433,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0x6);   // SALU and VALU may cross
     }
   };
+  auto tile_pv = [&](const char* vt) __attribute__((always_inline)) { tile_pv_hook(vt, [] {}); };
 
   auto run_s = [&](const uint4* kt, int j0) __attribute__((always_inline)) {
     if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
@@ -563,9 +565,11 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
   } else if constexpr (WN == 1) {
     // One barrier per tile: K and V of tile t + 1 are issued together once
-    // the score products of tile t are done and waited for as it ends (issued
-    // as the tile starts, their LDS writes slowed the score products, which
-    // gate the rest of the tile: 3-4% on the prefill launches).
+    // the softmax of tile t is done and its first V^T reads are on their way
+    // (tile_pv_hook), and waited for as it ends.  Issued as the tile starts,
+    // their LDS writes slowed the score products, which gate the rest of the
+    // tile (3-4% on the prefill launches); issued after the first V^T reads
+    // they no longer delay those either (another ~2%).
     if (ntiles > 0) {
       fetch_pages(it.tile_begin);
       issue_part(Flag<true>{}, it.tile_begin, lds_k0);
@@ -596,23 +600,25 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const int j0 = it.tile_begin + t * NWG;
       // even tile: compute from buffer 0 while buffer 1 fills
       run_s(lds_k0, j0);
-      if (t + 1 < ntiles) {
-        issue_part(Flag<true>{}, j0 + NWG, lds_k1);
-        issue_part(Flag<false>{}, j0 + NWG, lds_v1);
-        if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
-      }
-      tile_pv(reinterpret_cast<const char*>(lds_v0));
+      tile_pv_hook(reinterpret_cast<const char*>(lds_v0), [&] {
+        if (t + 1 < ntiles) {
+          issue_part(Flag<true>{}, j0 + NWG, lds_k1);
+          issue_part(Flag<false>{}, j0 + NWG, lds_v1);
+          if (t + 2 < ntiles) fetch_pages(j0 + 2 * NWG);
+        }
+      });
       wait_all();
       __syncthreads();
       if (t + 1 >= ntiles) break;
       // odd tile: compute from buffer 1 while buffer 0 fills
       run_s(lds_k1, j0 + NWG);
-      if (t + 2 < ntiles) {
-        issue_part(Flag<true>{}, j0 + 2 * NWG, lds_k0);
-        issue_part(Flag<false>{}, j0 + 2 * NWG, lds_v0);
-        if (t + 3 < ntiles) fetch_pages(j0 + 3 * NWG);
-      }
-      tile_pv(reinterpret_cast<const char*>(lds_v1));
+      tile_pv_hook(reinterpret_cast<const char*>(lds_v1), [&] {
+        if (t + 2 < ntiles) {
+          issue_part(Flag<true>{}, j0 + 2 * NWG, lds_k0);
+          issue_part(Flag<false>{}, j0 + 2 * NWG, lds_v0);
+          if (t + 3 < ntiles) fetch_pages(j0 + 3 * NWG);
+        }
+      });
       wait_all();
       __syncthreads();
     }
