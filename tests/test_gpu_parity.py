@@ -119,6 +119,30 @@ def test_prefill_kernels_across_page_sizes(pk, d, page):
                              f"chunks={chunks}")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefill_row_tiles_with_padding_waves(pk, d):
+    """Last row tiles of every fill level: the prefill tile's waves that hold
+    only padding rows take their load-and-barrier loop and exit, and the rows
+    of the other waves (including a wave's partly filled 16-row blocks) must
+    still be exact.  Packed rows per (request, kv head) = 4 * qo_len:
+    4, 16, 36, 68, 100, 132 and 260 over 128-row tiles (64-row at head_dim 256),
+    with causal, windowed and non-causal masks and split chunks."""
+    rng = np.random.default_rng(4242 + d)
+    qo = [1, 4, 9, 17, 25, 33, 65]
+    kv = [q + int(rng.integers(0, 300)) for q in qo]
+    dtype = W.FP16 if d == 64 else W.BF16
+    for causal, w in ((True, -1), (True, 23), (False, 50)):
+        wl = W.build("padding_waves", qo, kv, 8, 2, d, 16, causal, w, dtype,
+                     seed=int(rng.integers(1 << 30)), poison=True)
+        ref_o, ref_lse = oracle_full(wl)
+        tensors = device_inputs(wl)
+        for chunks in (0, 2):
+            o, lse, p = run(pk, wl, tensors, tile=1, num_kv_chunks=chunks)
+            assert p.info["tile_rows"] == (64 if d == 256 else 128)
+            assert_close(o, lse, ref_o, ref_lse, wl.dtype,
+                         f"padding waves d={d} causal={causal} w={w} chunks={chunks}")
+
+
 def test_empty_batch(pk):
     p = pk.plan([0], [0], [], [], 4, 2, 64, 16, True, dtype=torch.float16)
     q = torch.zeros((0, 4, 64), dtype=torch.float16, device="cuda")
