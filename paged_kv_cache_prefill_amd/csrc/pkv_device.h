@@ -123,19 +123,25 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
 // two 8-element chunks.  Every E4M3 value is exact in bf16 and fp16.
 template <typename T>
 __device__ __forceinline__ void e4m3x16_to(uint4 in, uint4& lo, uint4& hi) {
+  // One instruction per two codes, straight to the 16-bit type (scale 1).
   const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-  T out[16];
+  uint32_t out[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
-    out[4 * i + 0] = static_cast<T>(a[0]);
-    out[4 * i + 1] = static_cast<T>(a[1]);
-    out[4 * i + 2] = static_cast<T>(b[0]);
-    out[4 * i + 3] = static_cast<T>(b[1]);
+    if constexpr (__is_same(T, __bf16)) {
+      out[2 * i] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false));  // bytes 0, 1
+      out[2 * i + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true));   // bytes 2, 3
+    } else {
+      out[2 * i] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[i], 1.0f, false));
+      out[2 * i + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[i], 1.0f, true));
+    }
   }
-  lo = *reinterpret_cast<const uint4*>(out);
-  hi = *reinterpret_cast<const uint4*>(out + 8);
+  lo = make_uint4(out[0], out[1], out[2], out[3]);
+  hi = make_uint4(out[4], out[5], out[6], out[7]);
 }
 // Loads through this pointer type are scalar (constant address space).
 typedef __attribute__((address_space(4))) const int32_t const_i32;

@@ -105,3 +105,35 @@ def test_fp8_refusals(pk):
     with pytest.raises(pk.PkvError, match="debug_gather|fp8"):
         kc, vc = W.e4m3_pools(w, 1)
         p.debug_gather(torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda())
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+@pytest.mark.parametrize("d,tile", [(64, 1), (64, 2), (128, 1), (128, 2), (256, 1)])
+def test_fp8_every_code_decodes_exactly(pk, dtype, d, tile):
+    """One visible key per request makes each output row that key's V row times
+    v_scale, exactly (the softmax weight is 1): every finite E4M3 code at every
+    byte position of a 16-byte load then comes out bit-exact in the query dtype,
+    on the prefill and on the short-query tile."""
+    B = 4096 // d                      # B * d / 16 = 256 (load, position) slots per byte lane
+    rng = np.random.default_rng(d * 7 + tile)
+    pages = rng.permutation(B).astype(np.int32)
+    n = np.arange(B)[:, None] * (d // 16) + np.arange(d)[None, :] // 16
+    codes = ((n + np.arange(d)[None, :] % 16) % 256).astype(np.uint8)   # [request, dim]
+    codes[(codes & 0x7F) == 0x7F] = 0                                   # the two NaN codes
+    vc = np.zeros((B, 1, 1, d), np.uint8)
+    vc[pages, 0, 0, :] = codes
+    kc = W.e4m3_codes(rng.standard_normal((B, 1, 1, d), dtype=np.float32))
+    ar = np.arange(B + 1, dtype=np.int32)
+    p = pk.plan(ar, ar, pages, np.ones(B, np.int32), 4, 1, d, 1, True, dtype=torch_dtype(dtype),
+                kv_dtype="fp8_e4m3", k_scale=KS, v_scale=VS, tile=tile)
+    q = torch.randn((B, 4, d), dtype=torch.float32).to(torch_dtype(dtype)).cuda()
+    o, lse = p.run(q, torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda())
+    torch.cuda.synchronize()
+    assert p.info["tile_rows"] in ((128, 64) if tile == 1 else (16, 32))   # the tile asked for
+    want = oracle.decode_e4m3(codes, VS)                                # exact in fp16 and bf16
+    got = o.double().cpu().numpy()
+    for h in range(4):
+        bad = np.nonzero(got[:, h, :] != want)
+        assert bad[0].size == 0, (f"head {h}: {bad[0].size} codes differ, first request "
+                                  f"{bad[0][0]} dim {bad[1][0]} code {codes[bad][0]:#04x}")
+    assert np.isfinite(lse.cpu().numpy()).all()
