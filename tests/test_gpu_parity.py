@@ -119,6 +119,42 @@ def test_prefill_kernels_across_page_sizes(pk, d, page):
                              f"chunks={chunks}")
 
 
+@pytest.mark.parametrize("page", [16, 3])
+def test_pages_beyond_4_gib_of_pool(pk, page):
+    """K/V pools larger than 4 GiB (an unreferenced NaN fill) with the used pages
+    scattered over both ends, so page offsets need more than 32 bits: both tile
+    shapes, the scalar (page 16) and per-lane (page 3) page-id paths, split chunks."""
+    w = W.build("bigpool", [5, 40, 4, 4], [300, 90, 517, 6], 8, 2, 128, page, True, -1, W.BF16,
+                seed=77, poison=True)
+    ref_o, ref_lse = oracle_full(w)
+    q, k_small, v_small = device_inputs(w)
+    page_bytes = page * 2 * 128 * 2
+    big = (4 << 30) // page_bytes + 4096                      # pool > 4 GiB per tensor
+    n = w.num_pages
+    far = np.arange(n) % 2 == 1                               # odd pages at the far end
+    remap = np.where(far, big - 1 - np.arange(n), np.arange(n)).astype(np.int64)
+    assert remap.max() * page_bytes >= (1 << 32)
+    idx = torch.from_numpy(remap).cuda()
+    k = torch.full((big, page, 2, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v = torch.full_like(k, float("nan"))
+    k[idx] = k_small
+    v[idx] = v_small
+    del k_small, v_small
+    a = w.plan_args()
+    a["kv_page_indices"] = remap[w.kv_page_indices].astype(np.int32)
+    try:
+        for tile in (1, 2):
+            for chunks in (0, 3):
+                p = pk.plan(**a, dtype=torch.bfloat16, tile=tile, num_kv_chunks=chunks)
+                o, lse = p.run(q, k, v)
+                torch.cuda.synchronize()
+                assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_lse, w.dtype,
+                             f"pool of {big} pages of {page} tile={tile} chunks={chunks}")
+    finally:
+        del k, v
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_prefill_row_tiles_with_padding_waves(pk, d):
     """Last row tiles of every fill level: the prefill tile's waves that hold
