@@ -126,6 +126,7 @@ typedef struct {
   int32_t has_device_copy;   /* 1 when built with a workspace (runnable) */
   int64_t int_ws_bytes;
   int64_t float_ws_bytes;
+  int64_t total_kv_len;      /* sum of the requests' kv_len (rows of a debug gather) */
 } pkv_plan_info;
 
 /*
@@ -133,7 +134,7 @@ typedef struct {
  * Arguments are those of pkv_plan.  Fails with the same refusals as pkv_plan.
  */
 pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                              const int32_t* kv_page_indices,
+                              const int32_t* kv_page_indices, int64_t num_indices,
                               const int32_t* kv_last_page_len, int32_t batch_size,
                               int32_t num_qo_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t page_size, int32_t causal,
@@ -144,33 +145,38 @@ pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr
  * plan: validate the batch and schedule it.
  *   qo_indptr[batch+1]   host; request b owns query rows [qo_indptr[b], qo_indptr[b+1]).
  *   kv_indptr[batch+1]   host; request b owns page-table entries [kv_indptr[b], kv_indptr[b+1]).
- *   kv_page_indices[kv_indptr[batch]]  host; physical page ids.
+ *   kv_page_indices[num_indices]  host; physical page ids.  num_indices must
+ *                        equal kv_indptr[batch] (the page table's length).
  *   kv_last_page_len[batch]  host; keys on the request's last page, in [1, page_size]
  *                        when it has a page.  kv_len = (pages - 1) * page_size + last.
  *   num_qo_heads / num_kv_heads: q head h reads kv head h / (num_qo_heads / num_kv_heads).
  *   head_dim in {64, 128, 256} (256: prefill tile only); page_size >= 1;
  *   causal 0/1 (bottom-right aligned);
- *   window_left >= -1 (-1 = no window); sm_scale finite; dtype PKV_FP16 or PKV_BF16.
+ *   window_left >= -1 (-1 = no window); sm_scale finite and > 0 (the kernels take
+ *   each row's maximum before scaling); dtype PKV_FP16 or PKV_BF16.
  *   int_ws / float_ws: device workspaces of at least the sizes pkv_workspace_size
  *   reports.  The plan writes its task list into int_ws (one async copy on
  *   `stream`) and run() keeps fp32 partial states in float_ws: both must stay
  *   allocated and otherwise untouched while the plan is in use.  int_ws = NULL
  *   with int_ws_bytes = 0 builds a host-only plan (inspectable, not runnable).
+ *   The upload is built outside stream capture: a runnable plan on a stream
+ *   that is capturing is refused (pkv_run may be captured).
  * Refused (no handle is returned, earlier plans stay valid): decreasing indptr,
- *   indptr[0] != 0, last_page_len out of range, negative page ids, head counts
- *   GQA cannot divide, head_dim not 64/128/256, window_left < -1, a causal request
+ *   indptr[0] != 0, kv_indptr[batch] != num_indices, last_page_len out of
+ *   range, negative page ids, head counts GQA cannot divide, head_dim not
+ *   64/128/256, window_left < -1, sm_scale <= 0 or not finite, a causal request
  *   with kv_len < qo_len, a request with query rows and no key, a too-small
- *   workspace.
+ *   workspace, a capturing stream.
  * On success *out_plan owns a copy of everything it needs; free it with
  * pkv_plan_destroy.
  */
 pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
-                    int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t page_size, int32_t causal,
-                    int32_t window_left, float sm_scale, pkv_dtype dtype,
-                    void* int_ws, size_t int_ws_bytes, void* float_ws,
-                    size_t float_ws_bytes, void* stream,
+                    const int32_t* kv_page_indices, int64_t num_indices,
+                    const int32_t* kv_last_page_len, int32_t batch_size,
+                    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t page_size, int32_t causal, int32_t window_left,
+                    float sm_scale, pkv_dtype dtype, void* int_ws, size_t int_ws_bytes,
+                    void* float_ws, size_t float_ws_bytes, void* stream,
                     const pkv_plan_options* opts, pkv_plan_t* out_plan);
 
 /*
@@ -181,10 +187,11 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
  *     combined K/V caches are all views of this with the right strides.
  *   o  [o_rows, num_qo_heads, head_dim] packed, in dtype; row r of request b is
  *     o[qo_indptr[b] + r].
- *   lse [o_rows, num_qo_heads] packed fp32, natural log; NULL to skip.
+ *   lse [lse_rows, num_qo_heads] packed fp32, natural log; NULL to skip
+ *     (lse_rows is then ignored).
  * Shapes are checked against the plan: heads, head_dim (q, k, v separately),
- * page_size and dtype must match; q_rows and o_rows are minimums (callers pad);
- * every referenced page id must be below k_pages and v_pages.
+ * page_size and dtype must match; q_rows, o_rows and lse_rows are minimums
+ * (callers pad); every referenced page id must be below k_pages and v_pages.
  */
 pkv_status pkv_run(pkv_plan_t plan,
                    const void* q, int64_t q_rows, int32_t q_heads, int32_t q_dim,
@@ -193,7 +200,8 @@ pkv_status pkv_run(pkv_plan_t plan,
                    int32_t k_dim, int64_t k_s_page, int64_t k_s_tok, int64_t k_s_head,
                    const void* v, int64_t v_pages, int32_t v_page_size, int32_t v_heads,
                    int32_t v_dim, int64_t v_s_page, int64_t v_s_tok, int64_t v_s_head,
-                   pkv_dtype dtype, void* o, int64_t o_rows, float* lse, void* stream);
+                   pkv_dtype dtype, void* o, int64_t o_rows, float* lse, int64_t lse_rows,
+                   void* stream);
 
 /*
  * merge_states: combine two partial attention states over disjoint key sets
@@ -286,10 +294,20 @@ pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
 size_t pkv_chain_speculative_sampling_workspace_size(int32_t batch_size, int32_t vocab_size);
 
 /*
- * debug_gather: write the logical K and V rows of every planned request,
- * [sum kv_len, kv_heads, head_dim] in request order, through the same page
- * address path the attention kernel reads (for bit-exact gather checks).
- * Arguments as in pkv_run; k_out / v_out are packed device buffers.
+ * debug_gather: the attention kernel's own page gathering, for bit-exact
+ * checks (PR #362, Review notes: kv_len and every key address come from the
+ * paged metadata; PR #399, What changed: token, page and head strides are
+ * honoured).  It launches the kernel pkv_run launches for this plan -- same
+ * task list, tile shape, page addressing, loads, waits and barriers -- but
+ * instead of attending, each K/V tile that lands in LDS is written out
+ * (un-swizzled) to k_out / v_out, packed [total_kv_len, kv_heads, head_dim]
+ * in request order (request b's key j at row kv_out_start(b) + j, where
+ * kv_out_start(b) is the sum of the kv_len of the requests before it).
+ * Keys that no task of the plan loads (outside every row's causal / window
+ * band, or outside a kv_begin / kv_end range) are left untouched, so the
+ * caller pre-fills the outputs.  FP8 E4M3 caches give the decoded codes
+ * (without k_scale / v_scale) in the plan's dtype.  Arguments as in pkv_run
+ * (the plan's dtype); out_rows >= pkv_plan_info.total_kv_len.
  */
 pkv_status pkv_debug_gather(pkv_plan_t plan,
                             const void* k, int64_t k_pages, int32_t k_page_size,

@@ -64,7 +64,8 @@ class _PlanInfo(ctypes.Structure):
                 ("num_merge_items", ctypes.c_int32), ("num_partial_slots", ctypes.c_int32),
                 ("tile_rows", ctypes.c_int32), ("tile_keys", ctypes.c_int32),
                 ("max_page_index", ctypes.c_int32), ("has_device_copy", ctypes.c_int32),
-                ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64)]
+                ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64),
+                ("total_kv_len", ctypes.c_int64)]
 
 
 def library_path():
@@ -85,16 +86,16 @@ def load_library():
     pi32 = ctypes.POINTER(ctypes.c_int32)
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
-    lib.pkv_workspace_size.argtypes = [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32, i32, i32,
-                                       ctypes.POINTER(_PlanOptions), ctypes.POINTER(sz),
+    lib.pkv_workspace_size.argtypes = [pi32, pi32, pi32, i64, pi32, i32, i32, i32, i32, i32, i32,
+                                       i32, ctypes.POINTER(_PlanOptions), ctypes.POINTER(sz),
                                        ctypes.POINTER(sz)]
-    lib.pkv_plan.argtypes = [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32, i32, i32,
+    lib.pkv_plan.argtypes = [pi32, pi32, pi32, i64, pi32, i32, i32, i32, i32, i32, i32, i32,
                              ctypes.c_float, ctypes.c_int, vp, sz, vp, sz, vp,
                              ctypes.POINTER(_PlanOptions), ctypes.POINTER(vp)]
     lib.pkv_run.argtypes = [vp, vp, i64, i32, i32, i64, i64,
                             vp, i64, i32, i32, i32, i64, i64, i64,
                             vp, i64, i32, i32, i32, i64, i64, i64,
-                            ctypes.c_int, vp, i64, vp, vp]
+                            ctypes.c_int, vp, i64, vp, i64, vp]
     lib.pkv_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     lib.pkv_debug_gather.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, i64,
                                      vp, i64, i32, i32, i32, i64, i64, i64,
@@ -200,10 +201,8 @@ def _plan_arrays(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len):
     if batch < 0 or len(kv) != batch + 1 or len(last) != batch:
         raise PkvError(PKV_EINVAL, f"qo_indptr / kv_indptr / kv_last_page_len: expected lengths "
                                    f"B+1, B+1, B; given {len(qo)}, {len(kv)}, {len(last)}")
-    n = int(kv[-1]) if batch > 0 else 0
-    if idx is None or len(idx) < n:
-        raise PkvError(PKV_EINVAL, f"kv_page_indices: expected {n} entries (kv_indptr[-1]), "
-                                   f"given {0 if idx is None else len(idx)}")
+    if idx is None:
+        idx = np.zeros(0, dtype=np.int32)
     return qo, kv, idx, last, batch
 
 
@@ -216,8 +215,8 @@ def workspace_size(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_
                                             kv_last_page_len)
     ib, fb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     o = _options(**opts)
-    _check(lib.pkv_workspace_size(_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), _ptr_i32(last),
-                                  batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+    _check(lib.pkv_workspace_size(_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), len(idx),
+                                  _ptr_i32(last), batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                   int(bool(causal)), int(window_left), ctypes.byref(o),
                                   ctypes.byref(ib), ctypes.byref(fb)))
     return ib.value, fb.value
@@ -312,8 +311,7 @@ class Plan:
         if lse is None and return_lse:
             lse = torch.empty((rows, self.num_qo_heads), dtype=torch.float32, device=self.device)
         elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                                  or lse.dim() != 2 or lse.shape[1] != self.num_qo_heads
-                                  or lse.shape[0] < rows):
+                                  or lse.dim() != 2 or lse.shape[1] != self.num_qo_heads):
             raise PkvError(PKV_ELAYOUT, "lse: expected a packed fp32 [rows, num_qo_heads] tensor")
         code = _dtype_code(self.dtype)
         _check(_lib.pkv_run(
@@ -323,25 +321,37 @@ class Plan:
             v.data_ptr(), v.shape[0], v.shape[1], v.shape[2], v.shape[3],
             v.stride(0), v.stride(1), v.stride(2),
             code, out.data_ptr(), out.shape[0], lse.data_ptr() if lse is not None else None,
-            self._stream(stream)))
+            lse.shape[0] if lse is not None else 0, self._stream(stream)))
         return out, lse
 
-    def debug_gather(self, paged_k, paged_v, kv_layout="NHD", stream=None):
-        """Logical K and V rows [sum kv_len, Hkv, D] read through the kernel's page path."""
+    def debug_gather(self, paged_k, paged_v, kv_layout="NHD", k_out=None, v_out=None,
+                     stream=None):
+        """The attention kernel's own page gathering: logical K and V rows
+        [sum kv_len, Hkv, D] as the kernel loads them for this plan (FP8 caches:
+        decoded codes in the plan's dtype).  Keys no task of the plan loads are
+        left as they are in k_out / v_out (allocated uninitialised if None)."""
         torch = _torch()
         k = self._cache_view(paged_k, kv_layout)
         v = self._cache_view(paged_v, kv_layout)
-        total = int(self._kv_total)
-        ko = torch.empty((total, self.num_kv_heads, self.head_dim), dtype=self.dtype,
-                         device=self.device)
-        vo = torch.empty_like(ko)
+        total = int(self.info["total_kv_len"])
+        shape = (total, self.num_kv_heads, self.head_dim)
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=self.dtype, device=self.device)
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=self.dtype, device=self.device)
+        for name, t in (("k_out", k_out), ("v_out", v_out)):
+            if t.dtype != self.dtype or not t.is_contiguous() or t.dim() != 3 or \
+                    tuple(t.shape[1:]) != shape[1:]:
+                raise PkvError(PKV_ELAYOUT, f"{name}: expected a packed [rows, "
+                                            f"{shape[1]}, {shape[2]}] {self.dtype} tensor")
         _check(_lib.pkv_debug_gather(
             self._h, k.data_ptr(), k.shape[0], k.shape[1], k.shape[2], k.shape[3],
             k.stride(0), k.stride(1), k.stride(2),
             v.data_ptr(), v.shape[0], v.shape[1], v.shape[2], v.shape[3],
             v.stride(0), v.stride(1), v.stride(2),
-            _dtype_code(self.dtype), ko.data_ptr(), vo.data_ptr(), total, self._stream(stream)))
-        return ko, vo
+            _dtype_code(self.dtype), k_out.data_ptr(), v_out.data_ptr(),
+            min(k_out.shape[0], v_out.shape[0]), self._stream(stream)))
+        return k_out, v_out
 
 
 def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
@@ -354,7 +364,7 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
         sm_scale = 1.0 / math.sqrt(head_dim)
     code = _dtype_code(dtype)
     o = _options(**opts)
-    args = (_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), _ptr_i32(last), batch,
+    args = (_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), len(idx), _ptr_i32(last), batch,
             int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
             int(bool(causal)), int(window_left))
     handle = ctypes.c_void_p()
@@ -381,9 +391,6 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
     p = Plan(handle.value, tdtype, int(head_dim), int(num_qo_heads), int(num_kv_heads),
              int(page_size), dev, int_ws, float_ws)
     p.kv_fp8 = o.kv_dtype == PKV_FP8_E4M3
-    nb = np.diff(kv.astype(np.int64)) if batch > 0 else np.zeros(0, dtype=np.int64)
-    lens = np.where(nb > 0, (nb - 1) * int(page_size) + last.astype(np.int64), 0)
-    p._kv_total = int(lens.sum())
     return p
 
 

@@ -26,12 +26,16 @@ namespace pkv {
 // With PM 0 and 1 the last, partial tile of a task takes the general path.
 // VAR bit 0 adds the custom-mask test on edge tiles, bit 1 the logits
 // soft-cap, bit 2 FP8 K/V (register-staged, PM 0 or 3); each combination is
-// its own instantiation so the plain kernel carries none of them.
+// its own instantiation so the plain kernel carries none of them.  Bit 3 is
+// the gather check: the same task list, page addressing, loads, waits and
+// barriers, but instead of attending, every landed K/V tile is copied out of
+// LDS (un-swizzled) to a [sum kv_len, Hkv, D] array.
 template <typename T, int D, int WM, int WN, int QB, int NW, int WPE, int PM, int VAR>
 __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   constexpr bool kMask = (VAR & 1) != 0;   // custom topology mask
   constexpr bool kCap = (VAR & 2) != 0;    // logits soft-cap
   constexpr bool kFp8 = (VAR & 4) != 0;    // FP8 E4M3 K/V (converted into LDS)
+  constexpr bool kDump = (VAR & 8) != 0;   // copy the landed K/V tiles out instead
   // Short tiles on the scalar-page path bring Q in through LDS with the same
   // untracked direct loads as K and V, so the first key tiles load together
   // with it (the launcher takes this path only where Q's offsets within a
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const int pos = r / G;
       mrow[qb] += pos * rq.kv_len;
       const int h = it.kvh * G + (r - pos * G);
-      if constexpr (!kQL) {
+      if constexpr (!kQL && !kDump) {
         const T* src = qp + (int64_t)(rq.qo_start + pos) * a.q_s_tok + (int64_t)h * a.q_s_head;
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk)
@@ -389,7 +393,27 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
   };
 
-  auto tile_pv_hook = [&](const char* vt, auto&& hook) __attribute__((always_inline)) {
+  // Gather check: tile keys [j0, j0 + NWG) below kv_end (the rest were
+  // clamped re-reads of the last key) from LDS to out[kv_out_start + j][kvh].
+  auto dump_tile = [&](auto is_k, const uint4* t, int j0) __attribute__((always_inline)) {
+    constexpr bool IK = decltype(is_k)::value;
+    uint4* out = static_cast<uint4*>(IK ? a.gather_k : a.gather_v);
+    const int hkv = a.num_qo_heads / a.group;
+    for (int idx = tid; idx < NWG * CH; idx += 64 * NWAVE) {
+      const int r = idx / CH, c = idx % CH;
+      const int j = j0 + r;
+      if (j >= it.kv_end) continue;
+      const int pos = IK ? swz_k<CH>(r, c) : swz_v<CH>(r, c);
+      out[((int64_t)(rq.kv_out_start + j) * hkv + it.kvh) * CH + c] = t[r * CH + pos];
+    }
+  };
+
+  auto tile_pv_hook = [&](const char* vt, int j0, auto&& hook) __attribute__((always_inline)) {
+    if constexpr (kDump) {
+      dump_tile(Flag<false>{}, reinterpret_cast<const uint4*>(vt), j0);
+      hook();
+      return;
+    }
     // O^T += V^T P^T, 32 keys per MFMA.  B operand element e of lane
     // (g, l16) is key 4g+e (e < 4) or 16+4g+(e-4) of the 32-key step, where
     // S^T left them.  The A operand (V^T) comes from two transposing LDS
@@ -433,9 +457,15 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0x6);   // SALU and VALU may cross
     }
   };
-  auto tile_pv = [&](const char* vt) __attribute__((always_inline)) { tile_pv_hook(vt, [] {}); };
+  auto tile_pv = [&](const char* vt, int j0) __attribute__((always_inline)) {
+    tile_pv_hook(vt, j0, [] {});
+  };
 
   auto run_s = [&](const uint4* kt, int j0) __attribute__((always_inline)) {
+    if constexpr (kDump) {
+      dump_tile(Flag<true>{}, kt, j0);
+      return;
+    }
     if (j0 >= full_lo && j0 + NWG - 1 <= full_hi)
       tile_s(Flag<false>{}, kt, j0);
     else
@@ -444,7 +474,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // One LDS tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
   auto run_tile = [&](const uint4* kt, const uint4* vt, int j0) __attribute__((always_inline)) {
     run_s(kt, j0);
-    tile_pv(reinterpret_cast<const char*>(vt));
+    tile_pv(reinterpret_cast<const char*>(vt), j0);
   };
 
   if constexpr (kFp8) {
@@ -578,7 +608,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     }
     wait_all();
     __syncthreads();
-    if (wm * MW >= it.nrows || it.row0 + wm * MW >= R) {
+    if (!kDump && (wm * MW >= it.nrows || it.row0 + wm * MW >= R)) {
       // a wave holding only padding rows of the task's last row tile: it
       // issues its share of the loads and meets every barrier of the loop
       // below (one per tile), computes nothing, and has no row to write
@@ -600,7 +630,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const int j0 = it.tile_begin + t * NWG;
       // even tile: compute from buffer 0 while buffer 1 fills
       run_s(lds_k0, j0);
-      tile_pv_hook(reinterpret_cast<const char*>(lds_v0), [&] {
+      tile_pv_hook(reinterpret_cast<const char*>(lds_v0), j0, [&] {
         if (t + 1 < ntiles) {
           issue_part(Flag<true>{}, j0 + NWG, lds_k1);
           issue_part(Flag<false>{}, j0 + NWG, lds_v1);
@@ -612,7 +642,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       if (t + 1 >= ntiles) break;
       // odd tile: compute from buffer 1 while buffer 0 fills
       run_s(lds_k1, j0 + NWG);
-      tile_pv_hook(reinterpret_cast<const char*>(lds_v1), [&] {
+      tile_pv_hook(reinterpret_cast<const char*>(lds_v1), j0 + NWG, [&] {
         if (t + 2 < ntiles) {
           issue_part(Flag<true>{}, j0 + 2 * NWG, lds_k0);
           issue_part(Flag<false>{}, j0 + 2 * NWG, lds_v0);
@@ -648,7 +678,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
                         ((int64_t)(rq.qo_start + pos0) * a.q_s_tok) * (int64_t)sizeof(T);
     const int rlast = min(it.row0 + it.nrows, R) - 1;
 #pragma unroll
-    for (int i = wave * 64; i < QCH; i += 64 * NWAVE) {
+    for (int i = wave * 64; i < (kDump ? 0 : QCH); i += 64 * NWAVE) {   // no Q when gathering
       const int rr = (i + lane) / CH, c = (i + lane) % CH;
       const int r = min(it.row0 + rr, rlast);
       const int pos = r / G;
@@ -670,7 +700,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     if (ntiles > 1) wait_vm_lgkm0<NI>(); else wait_vm_lgkm0<0>();
     __syncthreads();
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < (kDump ? 0 : QB); ++qb) {
       const int rl = wm * MW + qb * 16 + l16;
       const bool valid = rl < it.nrows && it.row0 + rl < R;
 #pragma unroll
@@ -705,7 +735,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     if (t + 1 < ntiles) wait_vm_lgkm0<2 * NI>(); else wait_vm_lgkm0<0>();   // V(t) landed
     __syncthreads();
     if (t + 2 < ntiles) issue_part(Flag<true>{}, j0 + 2 * NWG, kc);        // K(t + 2)
-    tile_pv(reinterpret_cast<const char*>(vc));
+    tile_pv(reinterpret_cast<const char*>(vc), j0);
     if (t + 1 < ntiles) {
       if (t + 2 < ntiles) wait_vm_lgkm0<2 * NI>(); else wait_vm_lgkm0<NI>();  // K(t + 1) landed
       __syncthreads();
@@ -718,6 +748,8 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();   // the epilogue below reuses the buffers
   }   // FP8 / direct-load paths
+
+  if constexpr (kDump) return;   // the gather check writes no attention output
 
   // ---- epilogue
   // Row sums were kept per lane; reduce over the 4 lane groups sharing a row.

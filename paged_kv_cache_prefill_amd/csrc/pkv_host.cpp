@@ -287,11 +287,13 @@ void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_
 }
 
 pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
-                    int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int32_t page_size,
-                    int32_t causal, int32_t window_left, const pkv_plan_options* opts,
-                    Schedule* S) {
+                    const int32_t* kv_page_indices, int64_t num_indices,
+                    const int32_t* kv_last_page_len, int32_t batch, int32_t hq, int32_t hkv,
+                    int32_t head_dim, int32_t page_size, int32_t causal, int32_t window_left,
+                    const pkv_plan_options* opts, Schedule* S) {
   if (batch < 0) return fail(PKV_EINVAL, "batch_size: expected >= 0, given %d", batch);
+  if (num_indices < 0)
+    return fail(PKV_EINVAL, "num_indices: expected >= 0, given %lld", (long long)num_indices);
   if (hkv <= 0)
     return fail(PKV_EGQA, "num_kv_heads: expected a positive head count, given %d", hkv);
   if (hq <= 0 || hq % hkv != 0)
@@ -341,6 +343,12 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   const int32_t ki0 = batch > 0 ? kv_indptr[0] : 0;
   if (qi0 != 0) return fail(PKV_EINVAL, "qo_indptr[0]: expected 0, given %d", qi0);
   if (ki0 != 0) return fail(PKV_EINVAL, "kv_indptr[0]: expected 0, given %d", ki0);
+  // the page table must be exactly as long as kv_indptr says: the scheduler
+  // reads kv_indptr[batch] entries of it
+  const int64_t kv_n = batch > 0 ? kv_indptr[batch] : 0;
+  if (kv_n != num_indices)
+    return fail(PKV_EINVAL, "num_indices: expected kv_indptr[%d]=%lld page-table entries, given %lld",
+                batch, (long long)kv_n, (long long)num_indices);
 
   S->batch = batch;
   S->hq = hq;
@@ -400,7 +408,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (ms != PKV_OK) return ms;
   }
   S->total_q = batch > 0 ? qo_indptr[batch] : 0;
-  S->num_indices = batch > 0 ? kv_indptr[batch] : 0;
+  S->num_indices = num_indices;
   S->total_kv = kv_acc;
   if (S->num_indices > 0 && !kv_page_indices)
     return fail(PKV_EINVAL, "kv_page_indices: expected %lld entries, given NULL",
@@ -665,21 +673,22 @@ void put(std::vector<uint8_t>& k, const X* p, size_t n) {
 // Serialized scheduler inputs; empty when the arrays cannot be read (the
 // scheduler reports those errors itself).
 std::vector<uint8_t> schedule_key(const int32_t* qo, const int32_t* kv, const int32_t* idx,
-                                  const int32_t* last, int32_t batch, int32_t hq, int32_t hkv,
-                                  int32_t head_dim, int32_t page_size, int32_t causal,
-                                  int32_t window_left, const pkv_plan_options* opts) {
+                                  int64_t num_indices, const int32_t* last, int32_t batch,
+                                  int32_t hq, int32_t hkv, int32_t head_dim, int32_t page_size,
+                                  int32_t causal, int32_t window_left,
+                                  const pkv_plan_options* opts) {
   std::vector<uint8_t> k;
   if (batch < 0 || (batch > 0 && (!qo || !kv || !last))) return k;
+  if (num_indices < 0 || (num_indices > 0 && !idx)) return k;
   const int32_t sc[8] = {batch, hq, hkv, head_dim, page_size, causal, window_left, 0};
   put(k, sc, 8);
+  put(k, &num_indices, 1);
   if (batch > 0) {
     put(k, qo, (size_t)batch + 1);
     put(k, kv, (size_t)batch + 1);
     put(k, last, (size_t)batch);
-    const int64_t n = kv[batch] - kv[0];
-    if (n < 0 || (n > 0 && !idx)) return {};
-    put(k, idx, (size_t)n);
   }
+  put(k, idx, (size_t)num_indices);
   if (opts) {
     pkv_plan_options o = *opts;
     o.custom_mask = nullptr;
@@ -717,23 +726,24 @@ const char* pkv_last_error(void) { return g_err.c_str(); }
 const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
 
 pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                              const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
-                              int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t page_size, int32_t causal,
-                              int32_t window_left, const pkv_plan_options* opts,
-                              size_t* int_ws_bytes, size_t* float_ws_bytes) {
+                              const int32_t* kv_page_indices, int64_t num_indices,
+                              const int32_t* kv_last_page_len, int32_t batch_size,
+                              int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t causal, int32_t window_left,
+                              const pkv_plan_options* opts, size_t* int_ws_bytes,
+                              size_t* float_ws_bytes) {
   g_err.clear();
   g_pending.valid = false;
   Schedule S;
-  pkv_status st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
-                           num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
-                           opts, &S);
+  pkv_status st = schedule(qo_indptr, kv_indptr, kv_page_indices, num_indices, kv_last_page_len,
+                           batch_size, num_qo_heads, num_kv_heads, head_dim, page_size, causal,
+                           window_left, opts, &S);
   if (st != PKV_OK) return st;
   if (int_ws_bytes) *int_ws_bytes = S.int_bytes;
   if (float_ws_bytes) *float_ws_bytes = S.float_bytes;
-  g_pending.key = schedule_key(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len,
-                               batch_size, num_qo_heads, num_kv_heads, head_dim, page_size, causal,
-                               window_left, opts);
+  g_pending.key = schedule_key(qo_indptr, kv_indptr, kv_page_indices, num_indices,
+                               kv_last_page_len, batch_size, num_qo_heads, num_kv_heads, head_dim,
+                               page_size, causal, window_left, opts);
   if (!g_pending.key.empty()) {
     g_pending.S = std::move(S);
     g_pending.valid = true;
@@ -742,35 +752,38 @@ pkv_status pkv_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr
 }
 
 pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
-                    int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t page_size, int32_t causal, int32_t window_left,
-                    float sm_scale, pkv_dtype dtype, void* int_ws, size_t int_ws_bytes,
-                    void* float_ws, size_t float_ws_bytes, void* stream,
+                    const int32_t* kv_page_indices, int64_t num_indices,
+                    const int32_t* kv_last_page_len, int32_t batch_size, int32_t num_qo_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                    int32_t window_left, float sm_scale, pkv_dtype dtype, void* int_ws,
+                    size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes, void* stream,
                     const pkv_plan_options* opts, pkv_plan_t* out_plan) {
   g_err.clear();
   if (!out_plan) return fail(PKV_EINVAL, "out_plan: expected a pointer, given NULL");
   *out_plan = nullptr;
   if (dtype != PKV_FP16 && dtype != PKV_BF16)
     return fail(PKV_EINVAL, "dtype: expected fp16 or bf16, given %s", dtype_name(dtype));
-  if (!std::isfinite(sm_scale))
-    return fail(PKV_EINVAL, "sm_scale: expected a finite value, given %g", (double)sm_scale);
+  // The kernels take each row's maximum of the raw scores before scaling and
+  // give masked scores -inf before the scale: both assume sm_scale > 0.
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(PKV_EINVAL, "sm_scale: expected a finite value > 0, given %g", (double)sm_scale);
+  const bool dry = (int_ws == nullptr && int_ws_bytes == 0);
   pkv_plan_s* p = new pkv_plan_s();
   pkv_status st = PKV_OK;
   bool reused = false;
   if (g_pending.valid) {
     g_pending.valid = false;
-    if (schedule_key(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
-                     num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left,
-                     opts) == g_pending.key) {
+    if (schedule_key(qo_indptr, kv_indptr, kv_page_indices, num_indices, kv_last_page_len,
+                     batch_size, num_qo_heads, num_kv_heads, head_dim, page_size, causal,
+                     window_left, opts) == g_pending.key) {
       p->S = std::move(g_pending.S);
       reused = true;
     }
   }
   if (!reused)
-    st = schedule(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size,
-                  num_qo_heads, num_kv_heads, head_dim, page_size, causal, window_left, opts,
-                  &p->S);
+    st = schedule(qo_indptr, kv_indptr, kv_page_indices, num_indices, kv_last_page_len,
+                  batch_size, num_qo_heads, num_kv_heads, head_dim, page_size, causal,
+                  window_left, opts, &p->S);
   if (st != PKV_OK) {
     delete p;
     return st;
@@ -785,8 +798,23 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     p->v_scale = opts->v_scale > 0.f ? opts->v_scale : 1.f;
   }
   page_divider((uint32_t)page_size, &p->page_magic, &p->page_shift);
-  const bool dry = (int_ws == nullptr && int_ws_bytes == 0);
   if (!dry) {
+    // The task list is uploaded from a pinned staging buffer that is reused
+    // once an event recorded after the upload has completed.  Under stream
+    // capture that event is never recorded, so a captured upload could read a
+    // buffer another plan has refilled: plans are built outside capture.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t ce = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs);
+    if (ce != hipSuccess) {
+      delete p;
+      return fail(PKV_EHIP, "hipStreamIsCapturing: %s", hipGetErrorString(ce));
+    }
+    if (cs != hipStreamCaptureStatusNone) {
+      delete p;
+      return fail(PKV_EINVAL, "stream: expected a stream that is not capturing (plan runs "
+                              "outside graph capture; run() may be captured), given a "
+                              "capturing stream");
+    }
     if (!int_ws || int_ws_bytes < S.int_bytes) {
       delete p;
       return fail(PKV_EWORKSPACE, "int_ws: expected >= %zu bytes, given %zu%s", S.int_bytes,
@@ -845,6 +873,7 @@ pkv_status pkv_plan_get_info(pkv_plan_t p, pkv_plan_info* info) {
   info->has_device_copy = p->has_device_copy ? 1 : 0;
   info->int_ws_bytes = (int64_t)S.int_bytes;
   info->float_ws_bytes = (int64_t)S.float_bytes;
+  info->total_kv_len = S.total_kv;
   return PKV_OK;
 }
 
@@ -916,11 +945,9 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
                    int64_t k_s_tok, int64_t k_s_head, const void* v, int64_t v_pages,
                    int32_t v_page_size, int32_t v_heads, int32_t v_dim, int64_t v_s_page,
                    int64_t v_s_tok, int64_t v_s_head, pkv_dtype dtype, void* o, int64_t o_rows,
-                   float* lse, void* stream) {
+                   float* lse, int64_t lse_rows, void* stream) {
   g_err.clear();
   if (!p) return fail(PKV_ENOTPLANNED, "plan: run before a successful plan");
-  if (!p->has_device_copy)
-    return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
   const Schedule& S = p->S;
   if (dtype != p->dtype)
     return fail(PKV_EMISMATCH, "dtype: planned %s, given %s", dtype_name(p->dtype),
@@ -935,6 +962,9 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   if (o_rows < S.total_q)
     return fail(PKV_EMISMATCH, "o rows: planned at least %lld, given %lld", (long long)S.total_q,
                 (long long)o_rows);
+  if (lse != nullptr && lse_rows < S.total_q)
+    return fail(PKV_EMISMATCH, "lse rows: planned at least %lld, given %lld",
+                (long long)S.total_q, (long long)lse_rows);
   pkv_status st = check_cache(p, "k", k, k_pages, k_page_size, k_heads, k_dim, k_s_page, k_s_tok,
                               k_s_head);
   if (st != PKV_OK) return st;
@@ -955,10 +985,13 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
     return fail(PKV_ELAYOUT, "o: expected 16-byte alignment");
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(PKV_ELAYOUT, "lse: expected 4-byte alignment");
+  // every argument check above runs on host-only plans too (no device call)
+  if (!p->has_device_copy)
+    return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
   if (S.work.empty()) return PKV_OK;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  AttnArgs a;
+  AttnArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -1168,9 +1201,6 @@ pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_
                             void* stream) {
   g_err.clear();
   if (!p) return fail(PKV_ENOTPLANNED, "plan: debug_gather before a successful plan");
-  if (!p->has_device_copy)
-    return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
-  if (p->kv_fp8) return fail(PKV_EINVAL, "debug_gather: fp8_e4m3 caches are not gathered");
   const Schedule& S = p->S;
   if (dtype != p->dtype)
     return fail(PKV_EMISMATCH, "dtype: planned %s, given %s", dtype_name(p->dtype),
@@ -1187,26 +1217,35 @@ pkv_status pkv_debug_gather(pkv_plan_t p, const void* k, int64_t k_pages, int32_
     return fail(PKV_EINVAL, "k_out / v_out: expected device pointers, given NULL");
   if (reinterpret_cast<uintptr_t>(k_out) % 16 || reinterpret_cast<uintptr_t>(v_out) % 16)
     return fail(PKV_ELAYOUT, "k_out / v_out: expected 16-byte alignment");
-  GatherArgs g;
-  g.k = k;
-  g.v = v;
-  g.k_out = k_out;
-  g.v_out = v_out;
-  g.pages = reinterpret_cast<const int32_t*>(p->int_ws + S.off_pages);
-  g.reqs = reinterpret_cast<const ReqInfo*>(p->int_ws + S.off_reqs);
-  g.k_s_page = (uint32_t)k_s_page;
-  g.k_s_tok = (uint32_t)k_s_tok;
-  g.k_s_head = (uint32_t)k_s_head;
-  g.v_s_page = (uint32_t)v_s_page;
-  g.v_s_tok = (uint32_t)v_s_tok;
-  g.v_s_head = (uint32_t)v_s_head;
-  g.num_kv_heads = S.hkv;
-  g.page_size = S.page_size;
-  g.page_magic = p->page_magic;
-  g.page_shift = p->page_shift;
-  g.max_kv_len = S.max_kv_len;
-  g.batch = S.batch;
-  hipError_t e = launch_debug_gather((int)p->dtype, S.head_dim, g, static_cast<hipStream_t>(stream));
+  if (!p->has_device_copy)
+    return fail(PKV_ENOTPLANNED, "plan: built without a workspace (host-only), not runnable");
+  if (S.work.empty()) return PKV_OK;
+  // The attention kernel's own task list and load path (same tile kind, page
+  // addressing and schedule as pkv_run), copying each landed tile out.
+  AttnArgs a{};
+  a.k = k;
+  a.v = v;
+  a.pages = reinterpret_cast<const int32_t*>(p->int_ws + S.off_pages);
+  a.reqs = reinterpret_cast<const ReqInfo*>(p->int_ws + S.off_reqs);
+  a.work = reinterpret_cast<const WorkItem*>(p->int_ws + S.off_work);
+  a.k_s_page = (uint32_t)k_s_page;
+  a.k_s_tok = (uint32_t)k_s_tok;
+  a.k_s_head = (uint32_t)k_s_head;
+  a.v_s_page = (uint32_t)v_s_page;
+  a.v_s_tok = (uint32_t)v_s_tok;
+  a.v_s_head = (uint32_t)v_s_head;
+  a.num_work = (int32_t)S.work.size();
+  a.group = S.group;
+  a.num_qo_heads = S.hq;
+  a.page_size = S.page_size;
+  a.page_magic = p->page_magic;
+  a.page_shift = p->page_shift;
+  a.causal = S.causal;
+  a.kv_fp8 = p->kv_fp8 ? 1 : 0;
+  a.gather_k = k_out;
+  a.gather_v = v_out;
+  hipError_t e = launch_attention_dump(S.tile_kind, (int)p->dtype, S.head_dim, a,
+                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_EHIP, "debug gather launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }

@@ -100,6 +100,9 @@ struct AttnArgs {
   float cap_out;           // cap * log2(e)
   int32_t kv_fp8;          // 1: K/V are FP8 E4M3 codes (k_scale folded into scale_log2)
   float v_scale;           // FP8 V: value = code * v_scale
+  // gather check only: [sum kv_len, Hkv, D] outputs of the K and V tiles as loaded
+  void* gather_k;
+  void* gather_v;
 };
 
 struct SplitMergeArgs {
@@ -113,23 +116,6 @@ struct SplitMergeArgs {
   int32_t group;
   int32_t num_qo_heads;
   int32_t tile_rows;
-};
-
-struct GatherArgs {
-  const void* k;
-  const void* v;
-  void* k_out;
-  void* v_out;
-  const int32_t* pages;
-  const ReqInfo* reqs;
-  uint32_t k_s_page, k_s_tok, k_s_head;
-  uint32_t v_s_page, v_s_tok, v_s_head;
-  int32_t num_kv_heads;
-  int32_t page_size;
-  uint32_t page_magic;
-  uint32_t page_shift;
-  int32_t max_kv_len;
-  int32_t batch;
 };
 
 struct AppendArgs {
@@ -179,8 +165,10 @@ hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,
                                const void* o_b, const float* lse_b, void* o_out,
                                float* lse_out, int64_t rows, int32_t heads,
                                int32_t head_dim, hipStream_t stream);
-hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a,
-                               hipStream_t stream);
+// the gather check: the attention kernel's task list and loads, every landed
+// K/V tile copied out to a.gather_k / a.gather_v (plain or FP8 caches)
+hipError_t launch_attention_dump(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                 hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // bytes (a multiple of 16) from device-visible pinned host memory to device memory
 hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t stream);

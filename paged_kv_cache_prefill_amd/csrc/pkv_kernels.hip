@@ -18,9 +18,10 @@
 //     one GQA group, position-major) of one kv head.  Packing the group into
 //     the MFMA M dimension reads each K/V row once per kv head.
 //   * Keys are fetched straight through the page table: one 16-byte vector
-//     load per (key, 8 head-dim elements), coalesced along head_dim, staged
-//     through registers into a double-buffered LDS tile.  Nothing is gathered
-//     into a contiguous copy.
+//     load per (key, 8 head-dim elements), coalesced along head_dim, written
+//     by the load itself into a double-buffered LDS tile (global->LDS direct
+//     loads; FP8 caches are staged through registers and converted on the
+//     way in).  Nothing is gathered into a contiguous copy.
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_{bf16,f16} with fp32
 //     accumulation.  In that orientation each lane owns one query row (lane %
 //     16) in every MFMA result, so the row statistics stay per lane and the P
@@ -150,36 +151,6 @@ __global__ __launch_bounds__(256) void merge_o_kernel(const T* o_a, const float*
       out = (ta + tb) / (wa + wb);
     }
     o_out[idx] = from_f32<T>(out);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// debug gather: logical K/V rows through the attention kernel's address path
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-  constexpr int CH = D / 8;
-  const int b = blockIdx.y;
-  const ReqInfo rq = a.reqs[b];
-  const int j0 = blockIdx.x * 64;
-  if (j0 >= rq.kv_len) return;
-  const T* kp = static_cast<const T*>(a.k);
-  const T* vp = static_cast<const T*>(a.v);
-  T* ko = static_cast<T*>(a.k_out);
-  T* vo = static_cast<T*>(a.v_out);
-  const int total = 64 * a.num_kv_heads * CH;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int part = idx % CH;
-    const int h = (idx / CH) % a.num_kv_heads;
-    const int j = j0 + idx / (CH * a.num_kv_heads);
-    if (j >= rq.kv_len) continue;
-    const KeyLoc loc = locate_key(a.pages + rq.page_off, (uint32_t)j, a.page_magic, a.page_shift,
-                                  (uint32_t)a.page_size);
-    const uint64_t ks = key_offset(loc, a.k_s_page, a.k_s_tok, (uint32_t)h * a.k_s_head);
-    const uint64_t vs = key_offset(loc, a.v_s_page, a.v_s_tok, (uint32_t)h * a.v_s_head);
-    const int64_t dst = ((int64_t)(rq.kv_out_start + j) * a.num_kv_heads + h) * D + part * 8;
-    *reinterpret_cast<uint4*>(ko + dst) = *reinterpret_cast<const uint4*>(kp + ks + part * 8);
-    *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(vp + vs + part * 8);
   }
 }
 
@@ -327,26 +298,6 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (units == 0) return hipSuccess;
   const int64_t blocks = (units + 255) / 256 < 8192 ? (units + 255) / 256 : 8192;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_debug_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s) {
-  if (a.batch == 0 || a.max_kv_len == 0) return hipSuccess;
-  dim3 grid((a.max_kv_len + 63) / 64, a.batch);
-  if (dtype == 1 && head_dim == 128)
-    hipLaunchKernelGGL((gather_kernel<__bf16, 128>), grid, dim3(256), 0, s, a);
-  else if (dtype == 1 && head_dim == 64)
-    hipLaunchKernelGGL((gather_kernel<__bf16, 64>), grid, dim3(256), 0, s, a);
-  else if (dtype == 0 && head_dim == 128)
-    hipLaunchKernelGGL((gather_kernel<_Float16, 128>), grid, dim3(256), 0, s, a);
-  else if (dtype == 0 && head_dim == 64)
-    hipLaunchKernelGGL((gather_kernel<_Float16, 64>), grid, dim3(256), 0, s, a);
-  else if (dtype == 1 && head_dim == 256)
-    hipLaunchKernelGGL((gather_kernel<__bf16, 256>), grid, dim3(256), 0, s, a);
-  else if (dtype == 0 && head_dim == 256)
-    hipLaunchKernelGGL((gather_kernel<_Float16, 256>), grid, dim3(256), 0, s, a);
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

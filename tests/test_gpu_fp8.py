@@ -78,21 +78,10 @@ def test_fp8_fp16_queries(pk):
 def test_fp8_full_size(pk, case):
     w = W.config4(batch=64, num_kv_heads=8, values=True) if case == "verify_b64" else \
         W.config2(values=True)
-    kc, vc = W.e4m3_pools(w, 77, KS, VS)
+    kc, vc = W.e4m3_pools(w, 77, KS, VS, poison=True)
     o, lse, _ = _run(pk, w, kc, vc)
-    floats = _floats(w, kc, vc)
-    rng = np.random.default_rng(8)
-    a = w.plan_args()
-    del a["head_dim"]
-    for b in rng.choice(w.batch_size, size=min(6, w.batch_size), replace=False):
-        ql = int(w.qo_lens[b])
-        rows = sorted({0, ql - 1, int(rng.integers(ql))})
-        heads = [0, 31, int(rng.integers(32))]
-        ref_o, ref_lse = oracle.attention_rows(*floats, **a, b=int(b), rows=rows, heads=heads)
-        base = int(w.qo_indptr[b])
-        go = o[np.ix_([base + r for r in rows], heads)]
-        gl = lse[np.ix_([base + r for r in rows], heads)]
-        assert_close(go, gl, ref_o, ref_lse, w.dtype, f"fp8 {case} b={b}")
+    ref_o, ref_lse = _oracle(w, kc, vc)   # every output element
+    assert_close(o, lse, ref_o, ref_lse, w.dtype, f"fp8 {case}")
 
 
 def test_fp8_refusals(pk):
@@ -102,9 +91,6 @@ def test_fp8_refusals(pk):
     kb = to_device(w.k_pool, w.dtype)
     with pytest.raises(pk.PkvError, match="dtype"):
         p.run(q, kb, kb)
-    with pytest.raises(pk.PkvError, match="debug_gather|fp8"):
-        kc, vc = W.e4m3_pools(w, 1)
-        p.debug_gather(torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda())
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.FP16])

@@ -289,3 +289,100 @@ def test_sampling_refusals_on_host():
     assert call(2, 4, 5000, fake, 16) == pk.PKV_EWORKSPACE            # 2 x 5 tiles x 16 B needed
     assert call(2, 4, 5000, None, 1 << 20) == pk.PKV_EWORKSPACE
     assert call(2, 4, 5000, fake + 4, 1 << 20) == pk.PKV_ELAYOUT
+
+
+# ---------------------------------------------------------------------------
+# C-ABI refusals that the Python binding leaves to the library
+# ---------------------------------------------------------------------------
+def _c_plan_args(num_indices=None, sm_scale=0.125):
+    """pkv_plan arguments for _base() as ctypes values (host-only plan)."""
+    b = _base()
+    arr = lambda x: np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    qo, kv, idx, last = (arr(b["qo_indptr"]), arr(b["kv_indptr"]), arr(b["kv_page_indices"]),
+                         arr(b["kv_last_page_len"]))
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    n = len(idx) if num_indices is None else num_indices
+    keep = (qo, kv, idx, last)
+    head = (p32(qo), p32(kv), p32(idx), n, p32(last), 2, b["num_qo_heads"], b["num_kv_heads"],
+            b["head_dim"], b["page_size"], 1, -1)
+    return keep, head
+
+
+def _c_plan(num_indices=None, sm_scale=0.125):
+    lib = pk.load_library()
+    keep, head = _c_plan_args(num_indices)
+    h = ctypes.c_void_p()
+    st = lib.pkv_plan(*head, ctypes.c_float(sm_scale), pk.PKV_BF16, None, 0, None, 0, None,
+                      None, ctypes.byref(h))
+    return st, h, lib.pkv_last_error().decode()
+
+
+def test_c_abi_refuses_page_table_of_wrong_length():
+    """num_indices must equal kv_indptr[batch]: a short array would otherwise be
+    read past its end, a long one silently truncated (PR #399, What changed:
+    inputs the kernels would compute wrongly are refused before any compute)."""
+    lib = pk.load_library()
+    st, h, _ = _c_plan()
+    assert st == pk.PKV_OK and h.value
+    lib.pkv_plan_destroy(h)
+    for n in (4, 6, 0, -1):
+        st, h, msg = _c_plan(num_indices=n)
+        assert st == pk.PKV_EINVAL and not h.value, (n, msg)
+        assert "num_indices" in msg and f"given {n}" in msg, msg
+        if n >= 0:
+            assert "kv_indptr[2]=5" in msg, msg
+    keep, head = _c_plan_args(num_indices=3)
+    ib, fb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.pkv_workspace_size(*head, None, ctypes.byref(ib), ctypes.byref(fb)) == pk.PKV_EINVAL
+    assert "num_indices" in lib.pkv_last_error().decode()
+    # the binding passes the array's own length: a short or long list is refused too
+    for idx in ([3, 0, 1, 4], [3, 0, 1, 4, 2, 5]):
+        assert "num_indices" in refused("EINVAL", kv_page_indices=idx)
+
+
+def test_c_abi_refuses_non_positive_sm_scale():
+    """The kernels take each row's maximum before scaling: sm_scale must be > 0."""
+    for bad in (0.0, -0.125, float("nan"), float("inf")):
+        st, h, msg = _c_plan(sm_scale=bad)
+        assert st == pk.PKV_EINVAL and not h.value and "sm_scale" in msg, (bad, msg)
+    with pytest.raises(pk.PkvError, match="sm_scale"):
+        pk.plan_host(**_base(), sm_scale=-1.0)
+
+
+def test_c_abi_run_refuses_short_lse_and_rows():
+    """pkv_run checks q / o / lse rows (minimums) against the plan before anything
+    else; a host-only plan that passes every check is then not runnable.  The
+    pointers are never dereferenced: every refusal precedes any device call."""
+    lib = pk.load_library()
+    p = pk.plan_host(**_base(), dtype="bf16")
+    rows = p.info["total_q_rows"]
+    assert rows == 10 and p.info["total_kv_len"] == 21 + 48   # (2-1)*16+5, (3-1)*16+16
+    fake = 1 << 20   # 16-byte aligned, never read
+
+    def run(q_rows=rows, o_rows=rows, lse=fake, lse_rows=rows):
+        st = lib.pkv_run(p._h, fake, q_rows, 8, 128, 8 * 128, 128,
+                         fake, 5, 16, 2, 128, 16 * 2 * 128, 2 * 128, 128,
+                         fake, 5, 16, 2, 128, 16 * 2 * 128, 2 * 128, 128,
+                         pk.PKV_BF16, fake, o_rows, lse, lse_rows, None)
+        return st, lib.pkv_last_error().decode()
+
+    st, msg = run(lse_rows=rows - 1)
+    assert st == pk.PKV_EMISMATCH and "lse rows" in msg and "given 9" in msg, msg
+    st, msg = run(o_rows=rows - 1)
+    assert st == pk.PKV_EMISMATCH and "o rows" in msg, msg
+    st, msg = run(q_rows=rows - 1)
+    assert st == pk.PKV_EMISMATCH and "q rows" in msg, msg
+    # padded buffers and a skipped lse are fine (then only host-only-ness refuses)
+    for kw in ({"lse_rows": rows + 5, "o_rows": rows + 5, "q_rows": rows + 5},
+               {"lse": None, "lse_rows": 0}):
+        st, msg = run(**kw)
+        assert st == pk.PKV_ENOTPLANNED, msg
+
+
+def test_binding_computes_nothing_from_the_page_table():
+    """total_kv_len (the rows of a debug gather) comes from the library's plan."""
+    w = W.build("kvtotal", [3, 0, 5], [40, 17, 33], 4, 2, 64, 16, True, -1, W.BF16, seed=1,
+                values=False)
+    p = pk.plan_host(**w.plan_args())
+    assert p.info["total_kv_len"] == int(np.sum(w.kv_lens))
+    assert p.info["num_page_indices"] == len(w.kv_page_indices)
