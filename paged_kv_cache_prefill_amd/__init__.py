@@ -26,7 +26,7 @@ import os
 import numpy as np
 
 __all__ = ["plan", "plan_host", "verify_plan", "workspace_size", "merge_states", "append_kv",
-           "chain_speculative_sampling", "Plan",
+           "chain_speculative_sampling", "chain_speculative_sampling_no_alloc", "Plan",
            "PkvError", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +107,8 @@ def load_library():
                                   ctypes.c_int, vp, vp]
     lib.pkv_chain_speculative_sampling.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp,
                                                    vp, sz, vp]
+    lib.pkv_chain_speculative_sampling_no_alloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
+                                                            vp, vp, vp]
     lib.pkv_chain_speculative_sampling_workspace_size.argtypes = [i32, i32]
     lib.pkv_chain_speculative_sampling_workspace_size.restype = sz
     lib.pkv_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
@@ -115,7 +117,7 @@ def load_library():
     lib.pkv_plan_destroy.restype = None
     for name in ("pkv_workspace_size", "pkv_plan", "pkv_run", "pkv_merge_states",
                  "pkv_debug_gather", "pkv_append_kv", "pkv_chain_speculative_sampling",
-                 "pkv_plan_get_info",
+                 "pkv_chain_speculative_sampling_no_alloc", "pkv_plan_get_info",
                  "pkv_plan_get_work"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -534,16 +536,8 @@ def append_kv(append_k, append_v, batch_indices, positions, kv_indptr, kv_page_i
     return paged_k, paged_v
 
 
-def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accept_u, sample_u,
-                               out=None, num_accepted=None, workspace=None, stream=None):
-    """Accept/reject each request's draft chain -> (output_token_ids [B, n+1] int32,
-    num_accepted [B] int32).
-
-    draft_probs [B, n, V] and target_probs [B, n+1, V] float32, draft_token_ids
-    [B, n] int32, accept_u [B, n] and sample_u [B] float32 (uniforms in [0, 1)),
-    all packed on one device.  See include/pkv.h for the rule."""
+def _sampling_checks(draft_probs, draft_token_ids, target_probs, accept_u, sample_u):
     torch = _torch()
-    lib = load_library()
     if target_probs.dim() != 3:
         raise PkvError(PKV_EINVAL, "target_probs: expected [batch, n + 1, vocab]")
     B, n1, V = target_probs.shape
@@ -558,10 +552,35 @@ def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accep
         if t.dtype != dt or tuple(t.shape) != shape or t.device != dev or not t.is_contiguous():
             raise PkvError(PKV_EMISMATCH, f"{name}: expected a packed {dt} tensor {shape} on "
                                           f"{dev}, given {t.dtype} {tuple(t.shape)}")
+    return B, n, V, dev
+
+
+def _sampling_outputs(out, num_accepted, B, n, dev):
+    torch = _torch()
     if out is None:
         out = torch.empty((B, n + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    for name, t, shape in (("out", out, (B, n + 1)), ("num_accepted", num_accepted, (B,))):
+        if t.dtype != torch.int32 or tuple(t.shape) != shape or t.device != dev or \
+                not t.is_contiguous():
+            raise PkvError(PKV_EMISMATCH, f"{name}: expected a packed int32 tensor {shape}")
+    return out, num_accepted
+
+
+def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accept_u, sample_u,
+                               out=None, num_accepted=None, workspace=None, stream=None):
+    """Accept/reject each request's draft chain -> (output_token_ids [B, n+1] int32,
+    num_accepted [B] int32).
+
+    draft_probs [B, n, V] and target_probs [B, n+1, V] float32, draft_token_ids
+    [B, n] int32, accept_u [B, n] and sample_u [B] float32 (uniforms in [0, 1)),
+    all packed on one device.  See include/pkv.h for the rule."""
+    torch = _torch()
+    lib = load_library()
+    B, n, V, dev = _sampling_checks(draft_probs, draft_token_ids, target_probs, accept_u,
+                                    sample_u)
+    out, num_accepted = _sampling_outputs(out, num_accepted, B, n, dev)
     need = lib.pkv_chain_speculative_sampling_workspace_size(B, V)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -572,4 +591,25 @@ def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, accep
         accept_u.data_ptr(), sample_u.data_ptr(), B, n, V, out.data_ptr(),
         num_accepted.data_ptr(), workspace.data_ptr(), workspace.numel(),
         ctypes.c_void_p(stream.cuda_stream)))
+    return out, num_accepted
+
+
+def chain_speculative_sampling_no_alloc(draft_probs, draft_token_ids, target_probs, accept_u,
+                                        sample_u, out, num_accepted, stream=None):
+    """chain_speculative_sampling through the library's allocation-free entry point:
+    the caller passes the outputs, and the library keeps its tile sums in its own
+    per-GPU array (calls on one GPU must be ordered; see include/pkv.h)."""
+    torch = _torch()
+    lib = load_library()
+    B, n, V, dev = _sampling_checks(draft_probs, draft_token_ids, target_probs, accept_u,
+                                    sample_u)
+    if out is None or num_accepted is None:
+        raise PkvError(PKV_EINVAL, "out / num_accepted: expected caller-provided tensors")
+    out, num_accepted = _sampling_outputs(out, num_accepted, B, n, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(lib.pkv_chain_speculative_sampling_no_alloc(
+        draft_probs.data_ptr(), draft_token_ids.data_ptr(), target_probs.data_ptr(),
+        accept_u.data_ptr(), sample_u.data_ptr(), B, n, V, out.data_ptr(),
+        num_accepted.data_ptr(), ctypes.c_void_p(stream.cuda_stream)))
     return out, num_accepted

@@ -1140,15 +1140,16 @@ pkv_status pkv_append_kv(const void* append_k, int64_t ak_s_tok, int64_t ak_s_he
   return PKV_OK;
 }
 
-pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
-                                          const int32_t* draft_token_ids,
-                                          const float* target_probs, const float* accept_u,
-                                          const float* sample_u, int32_t batch,
-                                          int32_t num_speculate_tokens, int32_t vocab_size,
-                                          int32_t* output_token_ids, int32_t* num_accepted,
-                                          void* workspace, size_t workspace_bytes,
-                                          void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Arguments of both speculative-sampling entry points, checked on the host.
+pkv_status sampling_args(const float* draft_probs, const int32_t* draft_token_ids,
+                         const float* target_probs, const float* accept_u,
+                         const float* sample_u, int32_t batch, int32_t num_speculate_tokens,
+                         int32_t vocab_size, int32_t* output_token_ids, int32_t* num_accepted,
+                         SampleArgs* a) {
   if (batch < 0) return fail(PKV_EINVAL, "batch_size: expected >= 0, given %d", batch);
   if (num_speculate_tokens < 0)
     return fail(PKV_EINVAL, "num_speculate_tokens: expected >= 0, given %d", num_speculate_tokens);
@@ -1165,17 +1166,37 @@ pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
                           (const void*)num_accepted})
     if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0)
       return fail(PKV_ELAYOUT, "chain_speculative_sampling: expected 4-byte aligned pointers");
-  SampleArgs a;
-  a.draft_probs = draft_probs;
-  a.draft_ids = draft_token_ids;
-  a.target_probs = target_probs;
-  a.accept_u = accept_u;
-  a.sample_u = sample_u;
-  a.out_ids = output_token_ids;
-  a.num_accepted = num_accepted;
-  a.batch = batch;
-  a.num_spec = num_speculate_tokens;
-  a.vocab = vocab_size;
+  a->draft_probs = draft_probs;
+  a->draft_ids = draft_token_ids;
+  a->target_probs = target_probs;
+  a->accept_u = accept_u;
+  a->sample_u = sample_u;
+  a->out_ids = output_token_ids;
+  a->num_accepted = num_accepted;
+  a->batch = batch;
+  a->num_spec = num_speculate_tokens;
+  a->vocab = vocab_size;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
+                                          const int32_t* draft_token_ids,
+                                          const float* target_probs, const float* accept_u,
+                                          const float* sample_u, int32_t batch,
+                                          int32_t num_speculate_tokens, int32_t vocab_size,
+                                          int32_t* output_token_ids, int32_t* num_accepted,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  g_err.clear();
+  SampleArgs a{};
+  pkv_status st = sampling_args(draft_probs, draft_token_ids, target_probs, accept_u, sample_u,
+                                batch, num_speculate_tokens, vocab_size, output_token_ids,
+                                num_accepted, &a);
+  if (st != PKV_OK || batch == 0) return st;
   const size_t need = spec_sample_workspace_bytes(batch, vocab_size);
   if (!workspace || workspace_bytes < need)
     return fail(PKV_EWORKSPACE, "workspace: expected >= %zu bytes, given %zu%s", need,
@@ -1183,6 +1204,33 @@ pkv_status pkv_chain_speculative_sampling(const float* draft_probs,
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(PKV_ELAYOUT, "workspace: expected 16-byte alignment");
   hipError_t e = launch_spec_sample(a, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "speculative sampling launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+pkv_status pkv_chain_speculative_sampling_no_alloc(const float* draft_probs,
+                                                   const int32_t* draft_token_ids,
+                                                   const float* target_probs,
+                                                   const float* accept_u, const float* sample_u,
+                                                   int32_t batch, int32_t num_speculate_tokens,
+                                                   int32_t vocab_size, int32_t* output_token_ids,
+                                                   int32_t* num_accepted, void* stream) {
+  g_err.clear();
+  SampleArgs a{};
+  pkv_status st = sampling_args(draft_probs, draft_token_ids, target_probs, accept_u, sample_u,
+                                batch, num_speculate_tokens, vocab_size, output_token_ids,
+                                num_accepted, &a);
+  if (st != PKV_OK || batch == 0) return st;
+  const size_t need = spec_sample_workspace_bytes(batch, vocab_size);
+  if (need > kSpecScratchBytes)
+    return fail(PKV_EINVAL, "batch_size * ceil(vocab_size / 1024): expected <= %zu tiles of the "
+                            "library's %zu-byte scratch, given %d * %d = %zu tiles",
+                kSpecScratchBytes / 16, kSpecScratchBytes, batch, (vocab_size + 1023) / 1024,
+                need / 16);
+  void* ws = nullptr;   // the library's own per-device array: no allocation
+  hipError_t e = spec_sample_scratch(&ws);
+  if (e != hipSuccess) return fail(PKV_EHIP, "scratch address: %s", hipGetErrorString(e));
+  e = launch_spec_sample(a, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_EHIP, "speculative sampling launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }

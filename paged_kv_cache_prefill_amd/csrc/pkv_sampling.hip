@@ -21,10 +21,18 @@
 // read once, 4 or 8 bytes per vocabulary entry.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stdint.h>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
+
+// Tile-sum storage of the allocation-free entry point: each GPU the library
+// runs on holds one copy of this array until the process ends, shared by
+// every such call on that GPU (calls that overlap on one GPU race).  Host
+// code never names it directly: its device address comes from
+// hipGetSymbolAddress, per device (spec_sample_scratch below).
+static __device__ __align__(256) uint8_t scratch[pkv::kSpecScratchBytes];
 
 namespace pkv {
 
@@ -290,6 +298,27 @@ __global__ __launch_bounds__(kDrawThreads) void spec_draw_kernel(SampleArgs a, c
     if (tile < ntiles) pick = found != 0x7fffffff ? found : (tile_last >= 0 ? tile_last : lastpos);
     a.out_ids[(int64_t)b * (n + 1) + t] = pick >= 0 ? pick : V - 1;
   }
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t spec_sample_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 size_t spec_sample_workspace_bytes(int32_t batch, int32_t vocab) {

@@ -386,3 +386,19 @@ def test_binding_computes_nothing_from_the_page_table():
     p = pk.plan_host(**w.plan_args())
     assert p.info["total_kv_len"] == int(np.sum(w.kv_lens))
     assert p.info["num_page_indices"] == len(w.kv_page_indices)
+
+
+def test_no_alloc_sampling_refuses_sizes_beyond_its_array():
+    """The allocation-free sampling entry point holds its tile sums in a 4 MiB
+    array per GPU: batch * ceil(vocab / 1024) > 262144 tiles is refused before
+    any device call (the pointers are never dereferenced)."""
+    lib = pk.load_library()
+    fake = 1 << 20
+    call = lambda B, V: lib.pkv_chain_speculative_sampling_no_alloc(
+        fake, fake, fake, fake, fake, B, 4, V, fake, fake, None)
+    assert call(300, 1 << 20) == pk.PKV_EINVAL
+    msg = lib.pkv_last_error().decode()
+    assert "262144" in msg and "307200" in msg, msg
+    assert call(257, 1 << 20) == pk.PKV_EINVAL
+    assert call(0, 10) == pk.PKV_OK          # nothing to do
+    assert call(4, 0) == pk.PKV_EINVAL      # vocabulary out of range, as for the other entry
