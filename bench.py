@@ -9,8 +9,14 @@ pages needed, Hq 32 / Hkv 8, head_dim 128, bf16, causal.  Inputs are resident
 in HBM before the timed region.  value = algorithmic TFLOP/s over the whole
 step (4 * head_dim flops per visible (query, key) pair per q head).
 
+Inputs are cycled through device copies so that at least 512 MB of inputs is
+read between two uses of one copy (the 256 MB Infinity Cache serves none of a
+step's inputs).
+
 Prints ONE JSON line.  `roofline` covers the attention kernel: its average
-duration comes from HIP events around each launch on the stream it runs on.
+(and median) duration over >= 50 launches after 10 warm-ups, each launch
+bracketed by HIP events on the stream it runs on.  `plan_us` is the host cost
+of planning (the C-ABI call alone, and the Python binding's call).
 `coverage` times every other workload of the path (windowed prefill,
 non-causal windows at page 1024 and 16, speculative verify at every batch and
 kv-head count, long-context split-KV with merge) against its roofline.
@@ -122,24 +128,88 @@ def _device_inputs(w, dev):
     return conv(w.q), conv(w.k_pool), conv(w.v_pool)
 
 
-def time_kernel(pk, p, tensors, iters, warmup=3):
-    """Average run() duration (ms): one pair of HIP events on the launch stream
-    around `iters` back-to-back runs (the host enqueues far faster than the
-    kernel runs, so the stream never waits for it)."""
+def time_kernel(pk, p, copies, iters, warmup=10):
+    """run() durations (ms) on the stream it launches on, cycling through the
+    input copies (so every launch reads inputs no earlier launch has left in
+    the caches): `warmup` untimed launches, then `iters` launches each
+    bracketed by its own pair of HIP events.  Returns (mean, median, bracket):
+    bracket is one event pair around the same number of back-to-back launches
+    divided by their count (no per-launch event packets between them)."""
     import torch
     s = torch.cuda.current_stream()
-    q, k, v = tensors
-    o = torch.empty((p.total_q_rows, p.num_qo_heads, p.head_dim), dtype=p.dtype, device=q.device)
-    lse = torch.empty((p.total_q_rows, p.num_qo_heads), dtype=torch.float32, device=q.device)
-    for _ in range(warmup):
-        p.run(q, k, v, out=o, lse=lse)
+    q0 = copies[0][0]
+    o = torch.empty((p.total_q_rows, p.num_qo_heads, p.head_dim), dtype=p.dtype, device=q0.device)
+    lse = torch.empty((p.total_q_rows, p.num_qo_heads), dtype=torch.float32, device=q0.device)
+    for i in range(warmup):
+        p.run(*copies[i % len(copies)], out=o, lse=lse)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record(s)
+        p.run(*copies[i % len(copies)], out=o, lse=lse)
+        b.record(s)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(s)
-    for _ in range(iters):
-        p.run(q, k, v, out=o, lse=lse)
+    for i in range(iters):
+        p.run(*copies[i % len(copies)], out=o, lse=lse)
     b.record(s)
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters
+    return float(per.mean()), float(np.median(per)), a.elapsed_time(b) / iters
+
+
+def rotation_copies(tensors, touched_bytes, min_touched=512_000_000, max_copies=16):
+    """Device copies of (q, k, v) so that at least `min_touched` bytes of
+    inputs are read between two launches that use the same copy (the 256 MB
+    Infinity Cache then holds none of a launch's inputs)."""
+    n = max(1, min(max_copies, -(-min_touched // max(touched_bytes, 1))))
+    out = [tuple(tensors)]
+    for _ in range(n - 1):
+        out.append(tuple(t.clone() for t in tensors))
+    return out
+
+
+def plan_cost_us(pk, w, dt, dev, reps=50, **opts):
+    """Host cost of planning this workload, median over `reps` calls (us):
+    'c_abi' is pkv_plan alone through the C ABI (validation, scheduling and the
+    task-list upload launch; workspaces already allocated), 'python' is the
+    binding's plan() (sizing, two workspace allocations, pkv_plan)."""
+    import ctypes
+    import torch
+    lib = pk.load_library()
+    p0 = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
+    int_ws, float_ws = p0._int_ws, p0._float_ws
+    a = w.plan_args()
+    qo, kv, idx, last, batch = pk._plan_arrays(a["qo_indptr"], a["kv_indptr"],
+                                               a["kv_page_indices"], a["kv_last_page_len"])
+    o = pk._options(**{k: v for k, v in a.items() if k in ("custom_mask", "mask_indptr",
+                                                          "logits_soft_cap")}, **opts)
+    code = pk._dtype_code(dt)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (pk._ptr_i32(qo), pk._ptr_i32(kv), pk._ptr_i32(idx), len(idx), pk._ptr_i32(last),
+            batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, int(w.causal),
+            w.window_left, ctypes.c_float(w.sm_scale), code, int_ws.data_ptr(), int_ws.numel(),
+            float_ws.data_ptr(), float_ws.numel() * 4, stream, ctypes.byref(o))
+    h = ctypes.c_void_p()
+    c_times, py_times = [], []
+    torch.cuda.synchronize()
+    for i in range(reps + 5):
+        t0 = time.perf_counter()
+        st = lib.pkv_plan(*args, ctypes.byref(h))
+        t1 = time.perf_counter()
+        assert st == 0, lib.pkv_last_error()
+        lib.pkv_plan_destroy(h)
+        if i >= 5:
+            c_times.append((t1 - t0) * 1e6)
+    for i in range(reps + 5):
+        t0 = time.perf_counter()
+        pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
+        t1 = time.perf_counter()
+        if i >= 5:
+            py_times.append((t1 - t0) * 1e6)
+    torch.cuda.synchronize()
+    return {"c_abi": float(np.median(c_times)), "python": float(np.median(py_times))}
 
 
 def copy_ceiling(torch, dev, nbytes=1 << 30, iters=10):
@@ -165,11 +235,22 @@ def copy_ceiling(torch, dev, nbytes=1 << 30, iters=10):
 def cpu_baseline(w, budget_s=20.0):
     """The float64 oracle on requests of the workload, until ~budget_s of work."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "unknown")
+    except OSError:  # pragma: no cover
+        pass
     qf, kf, vf = w.float_inputs()
     order = np.argsort(w.qo_lens * w.kv_lens)   # cheapest requests first
     done, flops, t0 = [], 0.0, time.perf_counter()
@@ -190,7 +271,7 @@ def cpu_baseline(w, budget_s=20.0):
             break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "blas": blas, "blas_threads": int(threads),
             "sample": f"float64 numpy oracle over {len(done)} of {w.batch_size} requests "
                       f"(indices {sorted(done)}), all {w.num_qo_heads} q heads, {dt:.1f} s; "
                       f"host has {os.cpu_count()} logical CPUs"}
@@ -262,6 +343,35 @@ def coverage(pk, torch, dev, iters=20):
     rows any query row can see, plus q, o, lse) against the HBM peak.  K/V pools rotate so that at least 512 MB is touched
     between reuses of a pool (the 256 MB Infinity Cache cannot hold them)."""
     rows = []
+    for i, (name, w, opts) in enumerate(coverage_cases()):
+        dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+        kv_fp8 = opts.get("kv_dtype") == "fp8_e4m3"
+        nbytes = kv_bytes(w, 1 if kv_fp8 else 2)
+        copies = max(1, min(16, -(-512_000_000 // max(nbytes, 1))))
+        q, pools = _random_pools(w, dev, copies, seed=7000 + i, kv_fp8=kv_fp8)
+        p = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
+        eager_ms, ms = time_rotating(p, q, pools, iters)
+        flops = attention_flops(w)
+        # the roofline that binds: arithmetic intensity against the ridge point
+        hbm_bound = flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        rec = {"workload": name, "ms": ms, "eager_ms": eager_ms, "TFLOP/s": flops / ms / 1e9,
+               "GB/s": nbytes / ms / 1e6, "bound": "hbm" if hbm_bound else "mfma",
+               "pool_copies": copies, "work_items": p.info["num_work_items"],
+               "split_tiles": p.info["num_merge_items"]}
+        rec["frac"] = rec["GB/s"] / PEAK_HBM_GBS if hbm_bound else rec["TFLOP/s"] / PEAK_BF16_TFLOPS
+        rec["plan_us"] = plan_cost_us(pk, w, dt, dev, **opts)
+        rows.append(rec)
+        del q, pools, p
+        torch.cuda.empty_cache()
+    for name, w, per_req in (("append_prefill_b8", W.config2(values=False), None),
+                             ("append_verify_b64_hkv8", W.config4(batch=64, values=False), 4)):
+        rows.append(time_append(pk, torch, dev, name, w, per_req, iters))
+    rows.append(time_sampling(pk, torch, dev, iters))
+    return rows
+
+
+def coverage_cases():
+    """(name, workload without values, plan options) of every timed workload."""
     cases = [("single_contiguous_w-1", W.config1(values=False), {}),
              ("single_contiguous_w31", W.config1(window_left=31, values=False), {}),
              ("paged_prefill_b8_w127", W.config2(window_left=127, values=False), {})]
@@ -294,30 +404,7 @@ def coverage(pk, torch, dev, iters=20):
             cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",
                           W.config5(qo_len=ql, window_left=wl, values=False),
                           {"num_kv_chunks": W.CONFIG5_CHUNKS}))
-    for i, (name, w, opts) in enumerate(cases):
-        dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
-        kv_fp8 = opts.get("kv_dtype") == "fp8_e4m3"
-        nbytes = kv_bytes(w, 1 if kv_fp8 else 2)
-        copies = max(1, min(16, -(-512_000_000 // max(nbytes, 1))))
-        q, pools = _random_pools(w, dev, copies, seed=7000 + i, kv_fp8=kv_fp8)
-        p = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
-        eager_ms, ms = time_rotating(p, q, pools, iters)
-        flops = attention_flops(w)
-        # the roofline that binds: arithmetic intensity against the ridge point
-        hbm_bound = flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        rec = {"workload": name, "ms": ms, "eager_ms": eager_ms, "TFLOP/s": flops / ms / 1e9,
-               "GB/s": nbytes / ms / 1e6, "bound": "hbm" if hbm_bound else "mfma",
-               "pool_copies": copies, "work_items": p.info["num_work_items"],
-               "split_tiles": p.info["num_merge_items"]}
-        rec["frac"] = rec["GB/s"] / PEAK_HBM_GBS if hbm_bound else rec["TFLOP/s"] / PEAK_BF16_TFLOPS
-        rows.append(rec)
-        del q, pools, p
-        torch.cuda.empty_cache()
-    for name, w, per_req in (("append_prefill_b8", W.config2(values=False), None),
-                             ("append_verify_b64_hkv8", W.config4(batch=64, values=False), 4)):
-        rows.append(time_append(pk, torch, dev, name, w, per_req, iters))
-    rows.append(time_sampling(pk, torch, dev, iters))
-    return rows
+    return cases
 
 
 def time_sampling(pk, torch, dev, iters):
@@ -417,7 +504,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--window-left", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-coverage", action="store_true",
@@ -428,6 +515,10 @@ def main():
     ap.add_argument("--profile-verify", action="store_true",
                     help="short run for profilers of the verify workload instead (batch 64, "
                          "Hkv 8): 5 launches, one JSON line with its algorithmic bytes")
+    ap.add_argument("--profile-case", default=None,
+                    help="short run for profilers of one timed workload by name (see "
+                         "coverage_cases): 5 launches over rotating pools, one JSON line with "
+                         "its algorithmic bytes and flops")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB read + 256 MiB write elementwise kernel "
                          "(scale for the HBM byte counters)")
@@ -453,6 +544,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.profile_case:
+        found = [c for c in coverage_cases() if c[0] == args.profile_case]
+        if not found:
+            print(f"unknown workload {args.profile_case!r}; known: "
+                  f"{[c[0] for c in coverage_cases()]}", file=sys.stderr)
+            sys.exit(2)
+        name, w, opts = found[0]
+        kv_fp8 = opts.get("kv_dtype") == "fp8_e4m3"
+        nbytes = kv_bytes(w, 1 if kv_fp8 else 2)
+        ncopy = max(1, min(16, -(-512_000_000 // max(nbytes, 1))))
+        q, pools = _random_pools(w, dev, ncopy, seed=9100, kv_fp8=kv_fp8)
+        dt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+        p = pk.plan(**w.plan_args(), dtype=dt, device=dev, **opts)
+        ms, _ = time_rotating(p, q, pools, 5, warmup=1)
+        print(json.dumps({"workload": name, "algorithmic_bytes_per_launch": nbytes,
+                          "algorithmic_flops_per_launch": attention_flops(w),
+                          "work_items": p.info["num_work_items"],
+                          "split_tiles": p.info["num_merge_items"], "eager_ms": ms}))
+        return
+
     if args.profile_verify:
         w = W.config4(batch=64, num_kv_heads=8, values=False)
         q, pools = _random_pools(w, dev, 1, seed=7064)
@@ -463,27 +574,30 @@ def main():
         return
 
     w = W.config2(window_left=args.window_left)
-    tensors = _device_inputs(w, dev)
+    # copies of the inputs, cycled so that >= 512 MB of inputs is read between
+    # two uses of one copy (the Infinity Cache cannot serve a step's inputs)
+    copies = rotation_copies(_device_inputs(w, dev), kv_bytes(w))
     plan_args = w.plan_args()
     flops = attention_flops(w)
 
-    def step():
+    def step(i):
         p = pk.plan(**plan_args, dtype=torch.bfloat16, device=dev)
-        p.run(*tensors)
+        p.run(*copies[i % len(copies)])
         return p
 
-    for _ in range(args.warmup):
-        p = step()
+    for i in range(args.warmup):
+        p = step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        p = step()
+    for i in range(args.steps):
+        p = step(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt / args.steps * 1e3
     value = flops / (dt / args.steps) / 1e12
 
-    kernel_ms = time_kernel(pk, p, tensors, args.kernel_iters)
+    kernel_ms, kernel_median_ms, kernel_bracket_ms = time_kernel(
+        pk, p, copies, max(50, args.kernel_iters) if not args.profile else args.kernel_iters)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -494,11 +608,16 @@ def main():
                    "qo_len": "U[128,1024]", "kv_len": "qo + U[0,2048]", "page_size": w.page_size,
                    "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "causal": w.causal, "window_left": w.window_left,
-                   "total_q": w.total_q, "flops_per_step": flops},
+                   "total_q": w.total_q, "flops_per_step": flops,
+                   "input_copies": len(copies)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(),
-                     "kernel": "attn_kernel (prefill tile)", "kernel_ms": kernel_ms},
+                     "kernel": "attn_kernel (prefill tile)", "kernel_ms": kernel_ms,
+                     "kernel_median_ms": kernel_median_ms,
+                     "kernel_bracket_ms": kernel_bracket_ms,
+                     "frac_median": flops / (kernel_median_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "plan_us": plan_cost_us(pk, w, torch.bfloat16, dev) if not args.profile else None,
     }
     if not args.no_coverage:
         result["coverage"] = coverage(pk, torch, dev)

@@ -29,7 +29,7 @@ HIP_FLAGS = [
     # accumulators between AGPRs and VGPRs inside the key loop)
     "-mllvm", "-amdgpu-mfma-vgpr-form=true",
 ]
-HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
               "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
 
 

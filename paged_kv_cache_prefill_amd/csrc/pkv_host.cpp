@@ -136,6 +136,24 @@ pkv_status check_custom_mask(const pkv_plan_options& o, int32_t batch, int32_t c
   return PKV_OK;
 }
 
+struct RowTask {
+  int32_t b, kvh, row0, nrows;
+  int32_t key_lo, key_hi;  // inclusive visible key range of the task (key_lo > key_hi: none)
+  int32_t tile_begin;
+};
+
+// Temporaries of the scheduler, kept per thread so that their capacity is
+// reused from one plan to the next (a plan is otherwise dominated by
+// allocation and first-touch of these arrays).
+struct SchedScratch {
+  std::vector<int64_t> hist, rem, cnt, pieces, gcost;
+  std::vector<int32_t> start, gid, gorder, gxcd, costs;
+  std::vector<RowTask> tasks;
+  std::vector<WorkItem> items;
+  std::vector<std::pair<int32_t, int32_t>> chunks;
+};
+thread_local SchedScratch g_scr;
+
 // Chunk size (key tiles) for the automatic split of a launch with few tasks:
 // the candidate whose longest-first schedule over `slots` concurrent work
 // groups ends first, each work item costing its key tiles plus kItemTiles
@@ -145,43 +163,60 @@ pkv_status check_custom_mask(const pkv_plan_options& o, int32_t batch, int32_t c
 constexpr int64_t kItemTiles = 4;
 int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, int64_t min_tiles,
                            int64_t fallback) {
-  int64_t longest = 0;
-  for (int64_t c : pieces) longest = std::max(longest, c);
-  std::vector<int64_t> heap;   // slot loads, a min-heap
-  std::vector<int64_t> count;  // remainders by length (counting sort)
-  heap.reserve((size_t)slots);
+  int64_t longest = 0, total = 0;
+  for (int64_t n : pieces) {
+    longest = std::max(longest, n);
+    total += std::max<int64_t>(n, 0);
+  }
+  if (longest <= 0 || slots <= 0) return 0;
+  std::vector<int64_t>& hist = g_scr.hist;   // pieces by length
+  hist.assign((size_t)longest + 1, 0);
+  for (int64_t n : pieces)
+    if (n > 0) ++hist[(size_t)n];
+  std::vector<int64_t>& rem = g_scr.rem;     // remainders by length
+  std::vector<int64_t>& cnt = g_scr.cnt;     // slots by load (offset from the lowest initial load)
+  // Longest-first list schedule of the chunks of size c (c = 0: unsplit):
+  // full chunks first (all the same size: dealt out evenly), then the shorter
+  // remainders, longest first, each to a least loaded slot.  Loads only grow
+  // from the minimum, so the minimum never decreases: slots are counted per
+  // load value and a pointer walks up to the lowest occupied one, which gives
+  // the same makespan as a heap in time linear in pieces and load range.
   auto makespan = [&](int64_t c) {
-    // full chunks first (all the same size: dealt out evenly), then the
-    // shorter remainders, longest first, each to the least loaded slot
-    const int64_t len = c > 0 ? c : longest;
-    count.assign((size_t)len + 1, 0);
-    int64_t full = 0;
-    for (int64_t n : pieces) {
-      if (n <= 0) continue;
-      if (c > 0) {
-        full += n / c;
-        ++count[(size_t)(n % c)];
-      } else {
-        ++count[(size_t)n];
-      }
+    const int64_t len = c > 0 ? c - 1 : longest;
+    rem.assign((size_t)len + 1, 0);
+    int64_t full = 0, work = 0;
+    for (int64_t n = 1; n <= longest; ++n) {
+      const int64_t h = hist[(size_t)n];
+      if (h == 0) continue;
+      const int64_t r = c > 0 ? n % c : n;
+      if (c > 0) full += h * (n / c);
+      rem[(size_t)r] += h;
+      if (r > 0) work += h * (r + kItemTiles);
     }
     const int64_t per = c + kItemTiles, base = full / slots, extra = full % slots;
-    heap.clear();
-    for (int64_t i = 0; i < slots; ++i) heap.push_back((base + (i < extra ? 1 : 0)) * per);
+    const int64_t base_load = base * per;
     int64_t m = (base + (extra > 0 ? 1 : 0)) * per;
-    std::make_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+    // every assignment lands on a slot at most the average load above the
+    // lowest initial load, plus one item
+    const int64_t span = per + (work + slots - 1) / slots + len + kItemTiles + 2;
+    cnt.assign((size_t)span, 0);
+    cnt[0] = slots - extra;
+    if (extra > 0) cnt[(size_t)per] += extra;
+    int64_t lo = 0;
     for (int64_t r = len; r >= 1; --r) {
-      for (int64_t k = 0; k < count[(size_t)r]; ++k) {
-        std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
-        heap.back() += r + kItemTiles;
-        m = std::max(m, heap.back());
-        std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+      int64_t left = rem[(size_t)r];
+      while (left > 0) {
+        while (cnt[(size_t)lo] == 0) ++lo;
+        const int64_t t = std::min(left, cnt[(size_t)lo]);
+        const int64_t to = lo + r + kItemTiles;
+        cnt[(size_t)lo] -= t;
+        cnt[(size_t)to] += t;
+        m = std::max(m, base_load + to);
+        left -= t;
       }
     }
     return m;
   };
-  int64_t total = 0;
-  for (int64_t n : pieces) total += std::max<int64_t>(n, 0);
   // the even-share chunk size is kept unless the model expects a schedule at
   // least 10% shorter (its estimates are only that good)
   const int64_t fallback_m = makespan(fallback);
@@ -189,7 +224,7 @@ int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, in
   for (int64_t c : {4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128}) {
     if (c < min_tiles || c >= longest) continue;
     int64_t items = 0;   // far more items than slots never wins: skip those
-    for (int64_t n : pieces) items += (n + c - 1) / c;
+    for (int64_t n = 1; n <= longest; ++n) items += hist[(size_t)n] * ((n + c - 1) / c);
     if (items > 4 * slots) continue;
     // no schedule beats the average load: skip candidates that cannot win
     if ((total + items * kItemTiles + slots - 1) / slots >= best_m) continue;
@@ -202,11 +237,6 @@ int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, in
   return best_m * 10 <= fallback_m * 9 ? best : fallback;
 }
 
-struct RowTask {
-  int32_t b, kvh, row0, nrows;
-  int32_t key_lo, key_hi;  // inclusive visible key range of the task (key_lo > key_hi: none)
-  int32_t tile_begin;
-};
 
 // Work-group i of a launch runs on XCD i % 8, and each XCD has its own L2.
 // Tasks of one (request, kv head) read the same K/V rows, so when there are
@@ -218,72 +248,87 @@ struct RowTask {
 // made of short tasks.
 constexpr int kNumXcds = 8;
 
-void sort_longest_first(const std::vector<WorkItem>& items, const std::vector<int32_t>& costs,
-                        const std::vector<int32_t>& idx, std::vector<WorkItem>* out) {
-  int32_t max_cost = 0;
-  for (int32_t i : idx) max_cost = std::max(max_cost, costs[i]);
-  std::vector<int32_t> start(max_cost + 2, 0);
-  for (int32_t i : idx) ++start[max_cost - costs[i] + 1];
-  for (int32_t c = 1; c <= max_cost + 1; ++c) start[c] += start[c - 1];
-  out->assign(idx.size(), WorkItem{});
-  for (int32_t i : idx) (*out)[start[max_cost - costs[i]]++] = items[i];
-}
 
 void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_t>& costs,
-                    int32_t hkv, std::vector<WorkItem>* work) {
+                    int32_t batch, int32_t hkv, std::vector<WorkItem>* work) {
+  SchedScratch& T = g_scr;
   const size_t n = items.size();
-  std::vector<int32_t> all(n);
-  std::iota(all.begin(), all.end(), 0);
+  int32_t max_cost = 0;
+  for (int32_t c : costs) max_cost = std::max(max_cost, c);
   // group costs, keyed by request * hkv + kv head
-  std::vector<int64_t> gcost;
-  std::vector<int32_t> gid(n);
+  T.gcost.assign((size_t)batch * hkv, 0);
+  T.gid.resize(n);
   int64_t total = 0;
   for (size_t i = 0; i < n; ++i) {
-    gid[i] = items[i].b * hkv + items[i].kvh;
-    if ((size_t)gid[i] >= gcost.size()) gcost.resize(gid[i] + 1, 0);
-    gcost[gid[i]] += costs[i];
+    const int32_t g = items[i].b * hkv + items[i].kvh;
+    T.gid[i] = g;
+    T.gcost[g] += costs[i];
     total += costs[i];
   }
   int64_t groups = 0, gmax = 0;
-  for (int64_t c : gcost) {
+  for (int64_t c : T.gcost) {
     groups += c > 0;
     gmax = std::max(gmax, c);
   }
+  // positions of a stable sort by cost, largest first
+  T.start.assign((size_t)max_cost + 2, 0);
+  for (int32_t c : costs) ++T.start[max_cost - c + 1];
+  for (int32_t c = 1; c <= max_cost + 1; ++c) T.start[c] += T.start[c - 1];
   // Reuse exists only when a group has several query tiles (chunks of one
   // tile read disjoint keys).  Tasks of one tile are emitted consecutively.
   bool reuse = false;
   for (size_t i = 1; i < n && !reuse; ++i)
-    reuse = gid[i] == gid[i - 1] && items[i].row0 != items[i - 1].row0;
+    reuse = T.gid[i] == T.gid[i - 1] && items[i].row0 != items[i - 1].row0;
   if (!reuse || groups < 2 * kNumXcds || gmax * kNumXcds > total + total / 2) {
-    sort_longest_first(items, costs, all, work);
+    work->resize(n);
+    for (size_t i = 0; i < n; ++i) (*work)[T.start[max_cost - costs[i]]++] = items[i];
     return;
   }
-  std::vector<int32_t> gorder(gcost.size());
-  std::iota(gorder.begin(), gorder.end(), 0);
-  std::stable_sort(gorder.begin(), gorder.end(),
-                   [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
-  std::vector<int32_t> gxcd(gcost.size(), 0);
+  T.gorder.resize(T.gcost.size());
+  std::iota(T.gorder.begin(), T.gorder.end(), 0);
+  // largest group first, ties in group order
+  std::sort(T.gorder.begin(), T.gorder.end(), [&](int32_t a, int32_t b) {
+    return T.gcost[a] != T.gcost[b] ? T.gcost[a] > T.gcost[b] : a < b;
+  });
+  T.gxcd.assign(T.gcost.size(), 0);
   int64_t load[kNumXcds] = {0};
-  for (int32_t g : gorder) {
+  for (int32_t g : T.gorder) {
     int best = 0;
     for (int x = 1; x < kNumXcds; ++x)
       if (load[x] < load[best]) best = x;
-    gxcd[g] = best;
-    load[best] += gcost[g];
+    T.gxcd[g] = best;
+    load[best] += T.gcost[g];
   }
-  std::vector<int32_t> idx[kNumXcds];
-  for (size_t i = 0; i < n; ++i) idx[gxcd[gid[i]]].push_back((int32_t)i);
-  std::vector<WorkItem> lists[kNumXcds];
+  // each XCD's list in longest-first order (ties in task order): walk the
+  // tasks in the global stable order and deal each to its XCD's next slot
+  size_t len[kNumXcds] = {0};
+  for (size_t i = 0; i < n; ++i) ++len[T.gxcd[T.gid[i]]];
   size_t longest = 0;
-  for (int x = 0; x < kNumXcds; ++x) {
-    sort_longest_first(items, costs, idx[x], &lists[x]);
-    longest = std::max(longest, lists[x].size());
-  }
+  for (size_t l : len) longest = std::max(longest, l);
+  T.pieces.resize(n);   // task index at each sorted position
+  for (size_t i = 0; i < n; ++i) T.pieces[T.start[max_cost - costs[i]]++] = (int64_t)i;
   WorkItem empty{};  // num_rows 0: the kernel returns at once
   empty.slot = -1;
   work->assign(longest * kNumXcds, empty);
-  for (int x = 0; x < kNumXcds; ++x)
-    for (size_t k = 0; k < lists[x].size(); ++k) (*work)[k * kNumXcds + x] = lists[x][k];
+  size_t next[kNumXcds] = {0};
+  for (size_t k = 0; k < n; ++k) {
+    const size_t i = (size_t)T.pieces[k];
+    const int x = T.gxcd[T.gid[i]];
+    (*work)[next[x]++ * kNumXcds + x] = items[i];
+  }
+}
+
+// Smallest and largest page id (the plan scans every page-table entry; the
+// AVX2 clone does it 8 entries per instruction where the host has AVX2).
+__attribute__((target_clones("avx2", "default"))) void page_id_range(
+    const int32_t* __restrict ids, int64_t n, int32_t* lo, int32_t* hi) {
+  int32_t mn = *lo, mx = *hi;
+  for (int64_t i = 0; i < n; ++i) {
+    mn = std::min(mn, ids[i]);
+    mx = std::max(mx, ids[i]);
+  }
+  *lo = mn;
+  *hi = mx;
 }
 
 pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
@@ -320,7 +365,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   if (o.kv_end >= 0 && o.kv_end < o.kv_begin)
     return fail(PKV_EINVAL, "opts.kv_end: expected >= kv_begin=%d or < 0, given %d", o.kv_begin,
                 o.kv_end);
-  if (o.tile < 0 || o.tile > 2) return fail(PKV_EINVAL, "opts.tile: expected 0, 1 or 2, given %d", o.tile);
+  if (o.tile < 0 || o.tile > 2)
+    return fail(PKV_EINVAL, "opts.tile: expected 0, 1 or 2, given %d", o.tile);
   if (o.split_tiles < 0)
     return fail(PKV_EINVAL, "opts.split_tiles: expected >= 0, given %d", o.split_tiles);
   if (!(o.logits_soft_cap >= 0.f) || !std::isfinite(o.logits_soft_cap))
@@ -413,10 +459,16 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   if (S->num_indices > 0 && !kv_page_indices)
     return fail(PKV_EINVAL, "kv_page_indices: expected %lld entries, given NULL",
                 (long long)S->num_indices);
-  for (int64_t i = 0; i < S->num_indices; ++i) {
-    const int32_t p = kv_page_indices[i];
-    if (p < 0) return fail(PKV_EINVAL, "kv_page_indices[%lld]: expected >= 0, given %d", (long long)i, p);
-    S->max_page = std::max(S->max_page, p);
+  {
+    // one branch-free pass (min and max), then the first bad entry if any
+    int32_t pmin = INT32_MAX, pmax = -1;
+    page_id_range(kv_page_indices, S->num_indices, &pmin, &pmax);
+    if (S->num_indices > 0 && pmin < 0)
+      for (int64_t i = 0; i < S->num_indices; ++i)
+        if (kv_page_indices[i] < 0)
+          return fail(PKV_EINVAL, "kv_page_indices[%lld]: expected >= 0, given %d", (long long)i,
+                      kv_page_indices[i]);
+    S->max_page = pmax;
   }
 
   // ---- tile shape
@@ -432,7 +484,9 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   const int MR = S->rows, NK = S->keys, G = S->group;
 
   // ---- row tasks with their visible key ranges
-  std::vector<RowTask> tasks;
+  SchedScratch& T = g_scr;
+  std::vector<RowTask>& tasks = T.tasks;
+  tasks.clear();
   {
     int64_t n = 0;
     for (int32_t b = 0; b < batch; ++b) n += ((int64_t)S->reqs[b].qo_len * G + MR - 1) / MR;
@@ -473,8 +527,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   int64_t chunk_tiles = 0;  // 0: no automatic split
   {
     // pieces: the requested chunks each task's range meets, else the tasks
-    std::vector<int64_t> pieces;
-    pieces.reserve(tasks.size());
+    std::vector<int64_t>& pieces = T.pieces;
+    pieces.clear();
     for (const RowTask& t : tasks) {
       if (o.num_kv_chunks > 0 && t.key_lo <= t.key_hi) {
         const int64_t L = S->reqs[t.b].kv_len;
@@ -502,12 +556,11 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
       chunk_tiles = choose_chunk_tiles(pieces, per_cu * kNumCUs, min_tiles, even);
     }
   }
-  std::vector<WorkItem> items;
-  std::vector<int32_t> costs;
-  items.reserve(tasks.size() * 2);
-  costs.reserve(tasks.size() * 2);
-  std::vector<std::pair<int32_t, int32_t>> chunks;  // [c0, c1) key ranges of one task
-  chunks.reserve(64);
+  std::vector<WorkItem>& items = T.items;
+  std::vector<int32_t>& costs = T.costs;
+  items.clear();
+  costs.clear();
+  std::vector<std::pair<int32_t, int32_t>>& chunks = T.chunks;  // [c0, c1) ranges of one task
   auto emit = [&](const RowTask& t, int32_t lo, int32_t end, int32_t tb, int32_t slot) {
     WorkItem w;
     w.b = t.b;
@@ -574,7 +627,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   S->num_slots = slots;
   if (items.size() > (size_t)INT32_MAX / 2)
     return fail(PKV_EINVAL, "batch too large: %zu tasks", items.size());
-  order_for_xcds(items, costs, hkv, &S->work);
+  order_for_xcds(items, costs, batch, hkv, &S->work);
 
   // ---- workspace layouts
   size_t off = 0;
@@ -607,14 +660,17 @@ struct Staging {
 std::mutex g_staging_mu;
 std::vector<Staging*> g_staging;
 
-pkv_status copy_to_device(void* dst, const std::vector<uint8_t>& src, hipStream_t stream) {
+// Upload `bytes` (a multiple of 256) to dst on `stream`: `fill` writes them
+// straight into a free pinned staging buffer, which a copy kernel then reads.
+template <typename Fill>
+pkv_status copy_to_device(void* dst, size_t bytes, const Fill& fill, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(g_staging_mu);
   Staging* s = nullptr;
   for (Staging* c : g_staging) {
-    if (c->device != dev || c->cap < src.size()) continue;
+    if (c->device != dev || c->cap < bytes) continue;
     if (c->in_flight && hipEventQuery(c->ev) != hipSuccess) continue;
     s = c;
     break;
@@ -622,11 +678,11 @@ pkv_status copy_to_device(void* dst, const std::vector<uint8_t>& src, hipStream_
   if (!s) {
     s = new Staging();
     s->device = dev;
-    s->cap = std::max<size_t>(src.size(), 1 << 16);
+    s->cap = std::max<size_t>(bytes, 1 << 16);
     e = hipHostMalloc(&s->host, s->cap, hipHostMallocDefault);
     if (e != hipSuccess) {
       delete s;
-      return fail(PKV_EHIP, "hipHostMalloc(%zu): %s", src.size(), hipGetErrorString(e));
+      return fail(PKV_EHIP, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
     }
     e = hipHostGetDevicePointer(&s->dev_view, s->host, 0);
     if (e != hipSuccess) {
@@ -642,9 +698,8 @@ pkv_status copy_to_device(void* dst, const std::vector<uint8_t>& src, hipStream_
     }
     g_staging.push_back(s);
   }
-  std::memcpy(s->host, src.data(), src.size());
-  // src.size() is a multiple of 256 (the workspace layout is 256-byte aligned)
-  e = launch_upload(dst, s->dev_view, src.size(), stream);
+  fill(static_cast<uint8_t*>(s->host));
+  e = launch_upload(dst, s->dev_view, bytes, stream);
   if (e != hipSuccess) return fail(PKV_EHIP, "plan upload launch: %s", hipGetErrorString(e));
   e = hipEventRecord(s->ev, stream);
   if (e != hipSuccess) return fail(PKV_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -833,15 +888,22 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       delete p;
       return fail(PKV_ELAYOUT, "float_ws: expected 256-byte alignment");
     }
-    std::vector<uint8_t> blob(S.int_bytes, 0);
-    std::memcpy(blob.data() + S.off_reqs, S.reqs.data(), S.reqs.size() * sizeof(ReqInfo));
-    std::memcpy(blob.data() + S.off_work, S.work.data(), S.work.size() * sizeof(WorkItem));
-    std::memcpy(blob.data() + S.off_merge, S.merges.data(), S.merges.size() * sizeof(MergeItem));
-    if (S.num_indices > 0)
-      std::memcpy(blob.data() + S.off_pages, kv_page_indices, S.num_indices * sizeof(int32_t));
-    if (S.mask_bytes > 0)
-      std::memcpy(blob.data() + S.off_mask, opts->custom_mask, S.mask_bytes);
-    st = copy_to_device(int_ws, blob, static_cast<hipStream_t>(stream));
+    // the int workspace image: each region, then zeros up to the next one
+    auto fill = [&](uint8_t* dst) {
+      size_t at = 0;
+      auto put_region = [&](size_t off, const void* src, size_t n) {
+        std::memset(dst + at, 0, off - at);
+        if (n) std::memcpy(dst + off, src, n);
+        at = off + n;
+      };
+      put_region(S.off_reqs, S.reqs.data(), S.reqs.size() * sizeof(ReqInfo));
+      put_region(S.off_work, S.work.data(), S.work.size() * sizeof(WorkItem));
+      put_region(S.off_merge, S.merges.data(), S.merges.size() * sizeof(MergeItem));
+      put_region(S.off_pages, kv_page_indices, (size_t)S.num_indices * sizeof(int32_t));
+      put_region(S.off_mask, S.mask_bytes ? opts->custom_mask : nullptr, S.mask_bytes);
+      std::memset(dst + at, 0, S.int_bytes - at);
+    };
+    st = copy_to_device(int_ws, S.int_bytes, fill, static_cast<hipStream_t>(stream));
     if (st != PKV_OK) {
       delete p;
       return st;
