@@ -105,8 +105,9 @@ typedef struct {
      PKV_FP8_E4M3: one byte per element, OCP E4M3 (bias 7, no infinities,
      S.1111.111 NaN); key and value values are code * k_scale and
      code * v_scale (0 means 1).  Cache strides are then in bytes and must be
-     multiples of 16.  Not combinable with custom_mask or logits_soft_cap
-     (refused).  q and o stay in the pkv_run dtype. */
+     multiples of 16.  Combines with custom_mask and logits_soft_cap (the
+     capped logit is sm_scale * q.k over the decoded keys).  q and o stay in
+     the pkv_run dtype. */
   int32_t kv_dtype;
   float k_scale;
   float v_scale;

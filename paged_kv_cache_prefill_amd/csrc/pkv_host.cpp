@@ -376,8 +376,6 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     return fail(PKV_EINVAL, "opts.kv_dtype: expected 0 (the query dtype) or fp8_e4m3 (%d), given %d",
                 (int)PKV_FP8_E4M3, o.kv_dtype);
   if (o.kv_dtype == PKV_FP8_E4M3) {
-    if (o.custom_mask || o.logits_soft_cap > 0.f)
-      return fail(PKV_EINVAL, "opts.kv_dtype: fp8_e4m3 caches take no custom mask or soft-cap");
     for (float sc : {o.k_scale, o.v_scale})
       if (!(sc >= 0.f) || !std::isfinite(sc))
         return fail(PKV_EINVAL, "opts.k_scale / v_scale: expected finite values >= 0, given %g",
@@ -1085,7 +1083,8 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   a.scale_log2 = p->sm_scale * 1.4426950408889634f * (p->kv_fp8 ? p->k_scale : 1.f);
   a.kv_fp8 = p->kv_fp8 ? 1 : 0;
   a.v_scale = p->v_scale;
-  a.cap_in = p->soft_cap > 0.f ? p->sm_scale / p->soft_cap : 0.f;
+  // the kernel's raw score is q . codes; the logit is sm_scale * k_scale times it
+  a.cap_in = p->soft_cap > 0.f ? p->sm_scale * (p->kv_fp8 ? p->k_scale : 1.f) / p->soft_cap : 0.f;
   a.cap_out = p->soft_cap > 0.f ? p->soft_cap * 1.4426950408889634f : 0.f;
   hipError_t e = launch_attention(S.tile_kind, (int)p->dtype, S.head_dim, a, hs);
   if (e != hipSuccess) return fail(PKV_EHIP, "attention launch: %s", hipGetErrorString(e));

@@ -157,8 +157,15 @@ hipError_t launch_attention_cap(int tile_kind, int dtype, int head_dim, const At
                                 hipStream_t stream);
 hipError_t launch_attention_mask_cap(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
                                      hipStream_t stream);
+// FP8 E4M3 K/V caches: plain, custom mask, soft-cap, both
 hipError_t launch_attention_fp8(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
                                 hipStream_t stream);
+hipError_t launch_attention_fp8_mask(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                     hipStream_t stream);
+hipError_t launch_attention_fp8_cap(int tile_kind, int dtype, int head_dim, const AttnArgs& a,
+                                    hipStream_t stream);
+hipError_t launch_attention_fp8_mask_cap(int tile_kind, int dtype, int head_dim,
+                                         const AttnArgs& a, hipStream_t stream);
 hipError_t launch_split_merge(int dtype, int head_dim, const SplitMergeArgs& a,
                               hipStream_t stream);
 hipError_t launch_merge_states(int dtype, const void* o_a, const float* lse_a,

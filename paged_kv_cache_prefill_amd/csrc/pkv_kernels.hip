@@ -224,7 +224,12 @@ hipError_t launch_attention(int tile_kind, int dtype, int head_dim, const AttnAr
   // the custom-mask and soft-cap variants live in their own files (compiled
   // in parallel); the plain kernel is instantiated here
   const bool mask = a.mask != nullptr, cap = a.cap_out != 0.f;
-  if (a.kv_fp8) return launch_attention_fp8(tile_kind, dtype, head_dim, a, s);   // plain only
+  if (a.kv_fp8) {
+    if (mask && cap) return launch_attention_fp8_mask_cap(tile_kind, dtype, head_dim, a, s);
+    if (mask) return launch_attention_fp8_mask(tile_kind, dtype, head_dim, a, s);
+    if (cap) return launch_attention_fp8_cap(tile_kind, dtype, head_dim, a, s);
+    return launch_attention_fp8(tile_kind, dtype, head_dim, a, s);
+  }
   if (mask && cap) return launch_attention_mask_cap(tile_kind, dtype, head_dim, a, s);
   if (mask) return launch_attention_mask(tile_kind, dtype, head_dim, a, s);
   if (cap) return launch_attention_cap(tile_kind, dtype, head_dim, a, s);

@@ -1,7 +1,10 @@
 """FP8 E4M3 K/V caches on the GPU against the oracle (values = code x scale,
 decoded by the oracle from the format's definition): every head dim, page
 address path and tile shape, windows, split chunks, NaN-poisoned unreferenced
-codes, full-size verify and prefill on sampled rows."""
+codes, custom topology masks and logits soft-caps alone and together, and
+full-size verify and prefill compared on every output element."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -82,6 +85,55 @@ def test_fp8_full_size(pk, case):
     o, lse, _ = _run(pk, w, kc, vc)
     ref_o, ref_lse = _oracle(w, kc, vc)   # every output element
     assert_close(o, lse, ref_o, ref_lse, w.dtype, f"fp8 {case}")
+
+
+def _tree_fp8(rng, d, page, window, cap, batch):
+    prefixes = [int(x) for x in rng.integers(0, 300, size=batch)]
+    mats = [W.tree_topology_mask(p, W.random_tree_parents(rng, int(n)))
+            for p, n in zip(prefixes, rng.integers(1, 12, size=batch))]
+    w = W.build("fp8tree", [m.shape[0] for m in mats], [m.shape[1] for m in mats], 8, 2, d,
+                page, False, window, W.BF16, seed=int(rng.integers(1 << 30)))
+    w.custom_mask, w.mask_indptr = W.pack_custom_mask(mats)
+    w.logits_soft_cap = cap
+    return w
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("page", [1, 3, 16])
+@pytest.mark.parametrize("mask,cap", [(True, 0.0), (False, 1.5), (True, 2.0)])
+def test_fp8_mask_and_soft_cap(pk, d, page, mask, cap):
+    """Topology masks and soft-caps over E4M3 caches: the cap acts on the
+    decoded logit sm_scale * q . (code * k_scale), so a cap of 1.5 or 2 with
+    N(0, 1)-like logits bends most of them; every page path and tile shape."""
+    rng = np.random.default_rng(zlib.crc32(repr((d, page, mask, cap)).encode()))
+    for window in (-1, 7, 150):
+        if mask:
+            w = _tree_fp8(rng, d, page, window, cap, int(rng.integers(1, 5)))
+        else:
+            w = W.build("fp8cap", [1, 23, 70, 130], [40, 23, 190, 400], 8, 2, d, page, True,
+                        window, W.BF16, seed=int(rng.integers(1 << 30)))
+            w.logits_soft_cap = cap
+        kc, vc = W.e4m3_pools(w, int(rng.integers(1 << 30)), KS, VS)
+        ref_o, ref_lse = _oracle(w, kc, vc)
+        for tile in ((1,) if d == 256 else (1, 2)):
+            for chunks in (0, 3):
+                o, lse, _ = _run(pk, w, kc, vc, tile=tile, num_kv_chunks=chunks)
+                assert_close(o, lse, ref_o, ref_lse, w.dtype,
+                             f"fp8 d={d} P={page} mask={mask} cap={cap} w={window} "
+                             f"tile={tile} chunks={chunks}")
+
+
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_fp8_tree_verify_full_size(pk, cap):
+    """The tree-verify workload (B16, Hkv 8, 8-node trees after 512..8192-key
+    prefixes) over E4M3 caches, with and without a soft-cap, every element."""
+    w = W.tree_verify(batch=16, values=True)
+    w.logits_soft_cap = cap
+    kc, vc = W.e4m3_pools(w, 91, KS, VS, poison=True)
+    o, lse, p = _run(pk, w, kc, vc)
+    assert p.info["tile_rows"] == 32
+    ref_o, ref_lse = _oracle(w, kc, vc)
+    assert_close(o, lse, ref_o, ref_lse, w.dtype, f"fp8 tree verify cap={cap}")
 
 
 def test_fp8_refusals(pk):
