@@ -671,6 +671,9 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     // task re-read its last row), then K0, V0 and K1 before the first wait,
     // which leaves K1 in flight.  SGPR base: the task's first position; lane
     // offsets: (position - first) * s_tok + head * s_head + chunk, in bytes.
+    // LDS slot c of row rr holds chunk c ^ (rr % 8) (rows are a multiple of
+    // the bank width apart: the fragment reads below would otherwise take
+    // 16 rows from the same banks).
     constexpr int QCH = MW * WM * CH;               // 16-byte chunks of the Q rows
     static_assert(QCH % 64 == 0, "Q rows per wave instruction");
     const int pos0 = it.row0 / G;
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     const int rlast = min(it.row0 + it.nrows, R) - 1;
 #pragma unroll
     for (int i = wave * 64; i < (kDump ? 0 : QCH); i += 64 * NWAVE) {   // no Q when gathering
-      const int rr = (i + lane) / CH, c = (i + lane) % CH;
+      const int rr = (i + lane) / CH, c = ((i + lane) % CH) ^ (rr & 7);
       const int r = min(it.row0 + rr, rlast);
       const int pos = r / G;
       const int h = it.kvh * G + (r - pos * G);
@@ -705,7 +708,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       const bool valid = rl < it.nrows && it.row0 + rl < R;
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk)
-        qf[qb][dk] = valid ? __builtin_bit_cast(frag, lds_q[rl * CH + dk * 4 + g])
+        qf[qb][dk] = valid ? __builtin_bit_cast(frag, lds_q[rl * CH + ((dk * 4 + g) ^ (rl & 7))])
                            : __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0));
     }
   } else {
@@ -798,7 +801,10 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   } else {
     // Waves along keys hold partial states of the same rows: combine in LDS.
     static_assert(WM == 1, "key-split tiles use one row block");
-    // per-wave [MW][D] fp32 slices: waves 0..WN/2-1 in lds_k0, the rest in lds_k1
+    // per-wave [MW][D] fp32 slices: waves 0..WN/2-1 in lds_k0, the rest in lds_k1.
+    // The 16-byte chunk c of row r sits at chunk c ^ (r % 8) of the row: rows
+    // are a multiple of the 128-byte bank width apart, so the plain layout
+    // would put the 16 rows a wave writes at once in the same banks.
     auto red_o_of = [&](int w) -> float* {
       float* base = reinterpret_cast<float*>(w < WN / 2 ? lds_k0 : lds_k1);
       return base + (w % (WN / 2)) * MW * D;
@@ -826,7 +832,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 v = oacc[db][qb] * sc;
-        *reinterpret_cast<f32x4*>(red_o_of(wn) + rl * D + db * 16 + 4 * g) = v;
+        *reinterpret_cast<f32x4*>(red_o_of(wn) + rl * D + ((db * 4 + g) ^ (rl & 7)) * 4) = v;
       }
     }
     __syncthreads();
@@ -843,7 +849,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < WN; ++w) {
         lt += red_l[w * MW + rl] * fast_exp2(red_m[w * MW + rl] - mu);
-        acc += *reinterpret_cast<const f32x4*>(red_o_of(w) + rl * D + d4 * 4);
+        acc += *reinterpret_cast<const f32x4*>(red_o_of(w) + rl * D + (d4 ^ (rl & 7)) * 4);
       }
       const int r = it.row0 + rl;
       if (rl >= it.nrows || r >= R) continue;

@@ -337,6 +337,39 @@ def test_split_equals_unsplit(pk):
             assert_close(o, lse, ref_o, ref_lse, w.dtype, f"chunks={chunks} tile={tile}")
 
 
+@pytest.mark.parametrize("case", ["prefill_d128", "prefill_d64", "short16", "short32", "d256",
+                                  "many_slots"])
+def test_split_tiles_merged_in_every_run(pk, case):
+    """One plan with split query tiles on every tile shape (and up to 24
+    partial slots per tile), run three times with fresh values each time,
+    every output element against the oracle: each run must merge its own
+    partials (a merge reading the previous run's slots, or one that misses
+    a slot, shows up as a mismatch)."""
+    d, tile, hq, opts = {"prefill_d128": (128, 1, 16, dict(num_kv_chunks=3)),
+                         "prefill_d64": (64, 1, 16, dict(num_kv_chunks=5)),
+                         "short16": (128, 2, 4, dict(num_kv_chunks=4)),
+                         "short32": (128, 2, 16, dict(split_tiles=2)),
+                         "d256": (256, 1, 8, dict(num_kv_chunks=4)),
+                         "many_slots": (64, 2, 16, dict(split_tiles=1))}[case]
+    qo = [1, 4, 7, 16 if case == "short16" else 40, 0, 2]
+    kv = [900, 2500, 1300, 3000, 50, 3]
+    base = W.build("merge_runs", qo, kv, hq, 4, d, 16, True, -1, W.BF16, seed=31, values=False)
+    p = plan_for(pk, base, tile=tile, **opts)
+    assert p.info["num_merge_items"] > 0
+    assert p.info["tile_rows"] == {"short16": 16, "short32": 32, "many_slots": 32,
+                                   "d256": 64}.get(case, 128)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    pool = (base.num_pages, base.page_size, base.num_kv_heads, d)
+    for run_i in range(3):
+        w = W.Workload(**{**base.__dict__,
+                          "q": W.draw_values(rng, (base.total_q, hq, d), W.BF16),
+                          "k_pool": W.draw_values(rng, pool, W.BF16),
+                          "v_pool": W.draw_values(rng, pool, W.BF16)})
+        o, lse = p.run(*device_inputs(w))
+        torch.cuda.synchronize()
+        check_full(w, o.float().cpu().numpy(), lse.cpu().numpy(), f"{case} run {run_i}")
+
+
 def test_key_range_partial_state(pk):
     w = W.build("range", [6, 40], [100, 70], 4, 2, 128, 16, True, 10, W.BF16, seed=16)
     for a, e in ((0, 30), (30, 64), (64, 101), (90, 95)):
