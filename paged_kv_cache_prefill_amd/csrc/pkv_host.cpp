@@ -185,11 +185,15 @@ int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, in
     const int64_t len = c > 0 ? c - 1 : longest;
     rem.assign((size_t)len + 1, 0);
     int64_t full = 0, work = 0;
-    for (int64_t n = 1; n <= longest; ++n) {
+    // q, r: n / c and n % c, stepped along with n (no division per length)
+    for (int64_t n = 1, q = 0, r = 1; n <= longest; ++n, ++r) {
+      if (c > 0 && r == c) {
+        r = 0;
+        ++q;
+      }
       const int64_t h = hist[(size_t)n];
       if (h == 0) continue;
-      const int64_t r = c > 0 ? n % c : n;
-      if (c > 0) full += h * (n / c);
+      full += h * q;
       rem[(size_t)r] += h;
       if (r > 0) work += h * (r + kItemTiles);
     }
@@ -220,11 +224,21 @@ int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, in
   // the even-share chunk size is kept unless the model expects a schedule at
   // least 10% shorter (its estimates are only that good)
   const int64_t fallback_m = makespan(fallback);
-  int64_t best = 0, best_m = makespan(0);
+  // Only a candidate below both the unsplit schedule and the fallback can be
+  // returned, so the search starts from the lower of the two (same result).
+  int64_t best = 0, best_m = std::min(makespan(0), fallback_m);
   for (int64_t c : {4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128}) {
     if (c < min_tiles || c >= longest) continue;
+    // a full chunk exists (c < longest), so no schedule ends before one chunk
+    if (c + kItemTiles >= best_m) continue;
     int64_t items = 0;   // far more items than slots never wins: skip those
-    for (int64_t n = 1; n <= longest; ++n) items += hist[(size_t)n] * ((n + c - 1) / c);
+    for (int64_t n = 1, k = 1, r = 1; n <= longest; ++n, ++r) {   // k = ceil(n / c)
+      if (r > c) {
+        r = 1;
+        ++k;
+      }
+      items += hist[(size_t)n] * k;
+    }
     if (items > 4 * slots) continue;
     // no schedule beats the average load: skip candidates that cannot win
     if ((total + items * kItemTiles + slots - 1) / slots >= best_m) continue;
@@ -255,6 +269,21 @@ void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_
   const size_t n = items.size();
   int32_t max_cost = 0;
   for (int32_t c : costs) max_cost = std::max(max_cost, c);
+  // positions of a stable sort by cost, largest first
+  T.start.assign((size_t)max_cost + 2, 0);
+  for (int32_t c : costs) ++T.start[max_cost - c + 1];
+  for (int32_t c = 1; c <= max_cost + 1; ++c) T.start[c] += T.start[c - 1];
+  auto longest_first = [&] {
+    work->resize(n);
+    for (size_t i = 0; i < n; ++i) (*work)[T.start[max_cost - costs[i]]++] = items[i];
+  };
+  // Reuse exists only when a group has several query tiles (chunks of one
+  // tile read disjoint keys).  Tasks of one tile are emitted consecutively.
+  bool reuse = false;
+  for (size_t i = 1; i < n && !reuse; ++i)
+    reuse = items[i].b == items[i - 1].b && items[i].kvh == items[i - 1].kvh &&
+            items[i].row0 != items[i - 1].row0;
+  if (!reuse) return longest_first();
   // group costs, keyed by request * hkv + kv head
   T.gcost.assign((size_t)batch * hkv, 0);
   T.gid.resize(n);
@@ -270,20 +299,7 @@ void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_
     groups += c > 0;
     gmax = std::max(gmax, c);
   }
-  // positions of a stable sort by cost, largest first
-  T.start.assign((size_t)max_cost + 2, 0);
-  for (int32_t c : costs) ++T.start[max_cost - c + 1];
-  for (int32_t c = 1; c <= max_cost + 1; ++c) T.start[c] += T.start[c - 1];
-  // Reuse exists only when a group has several query tiles (chunks of one
-  // tile read disjoint keys).  Tasks of one tile are emitted consecutively.
-  bool reuse = false;
-  for (size_t i = 1; i < n && !reuse; ++i)
-    reuse = T.gid[i] == T.gid[i - 1] && items[i].row0 != items[i - 1].row0;
-  if (!reuse || groups < 2 * kNumXcds || gmax * kNumXcds > total + total / 2) {
-    work->resize(n);
-    for (size_t i = 0; i < n; ++i) (*work)[T.start[max_cost - costs[i]]++] = items[i];
-    return;
-  }
+  if (groups < 2 * kNumXcds || gmax * kNumXcds > total + total / 2) return longest_first();
   T.gorder.resize(T.gcost.size());
   std::iota(T.gorder.begin(), T.gorder.end(), 0);
   // largest group first, ties in group order
@@ -480,6 +496,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   S->rows = tile_rows(kind, head_dim);
   S->keys = tile_keys(kind, head_dim);
   const int MR = S->rows, NK = S->keys, G = S->group;
+  // key tiles are 32, 64 or 128 keys: key offsets (never negative) divide by shifts
+  const int nk_sh = __builtin_ctz((unsigned)NK);
 
   // ---- row tasks with their visible key ranges
   SchedScratch& T = g_scr;
@@ -509,7 +527,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
         hi = std::min<int64_t>(hi, opt_end - 1);
         t.key_lo = (int32_t)std::min<int64_t>(lo, INT32_MAX / 2);
         t.key_hi = (int32_t)std::max<int64_t>(hi, -1);
-        t.tile_begin = t.key_lo <= t.key_hi ? t.key_lo / NK * NK : 0;
+        t.tile_begin = t.key_lo <= t.key_hi ? (t.key_lo >> nk_sh) << nk_sh : 0;
         tasks.push_back(t);
       }
     }
@@ -520,7 +538,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   // into chunks of the size choose_chunk_tiles picks (partials are merged
   // either way)
   auto cost = [&](const RowTask& t) -> int64_t {
-    return t.key_lo > t.key_hi ? 0 : (t.key_hi + 1 - t.tile_begin + NK - 1) / NK;
+    return t.key_lo > t.key_hi ? 0 : (t.key_hi + 1 - t.tile_begin + NK - 1) >> nk_sh;
   };
   int64_t chunk_tiles = 0;  // 0: no automatic split
   {
@@ -531,11 +549,11 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
       if (o.num_kv_chunks > 0 && t.key_lo <= t.key_hi) {
         const int64_t L = S->reqs[t.b].kv_len;
         int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
-        clen = std::max<int64_t>(NK, (clen + NK - 1) / NK * NK);
+        clen = std::max<int64_t>(NK, ((clen + NK - 1) >> nk_sh) << nk_sh);
         for (int64_t c0 = t.key_lo / clen * clen; c0 <= t.key_hi; c0 += clen) {
           const int64_t a = std::max<int64_t>(c0, t.key_lo);
           const int64_t e = std::min<int64_t>(c0 + clen, (int64_t)t.key_hi + 1);
-          pieces.push_back(e > a ? (e - 1) / NK - a / NK + 1 : 0);
+          pieces.push_back(e > a ? ((e - 1) >> nk_sh) - (a >> nk_sh) + 1 : 0);
         }
       } else {
         pieces.push_back(cost(t));
@@ -570,10 +588,21 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     w.slot = slot;
     w.tile_begin = tb;
     items.push_back(w);
-    costs.push_back(end > tb ? (end - tb + NK - 1) / NK : 0);
+    costs.push_back(end > tb ? (end - tb + NK - 1) >> nk_sh : 0);
   };
   int32_t slots = 0;
+  const bool splitting = chunk_tiles > 0 || o.num_kv_chunks > 0;
+  items.reserve(tasks.size());
+  costs.reserve(tasks.size());
+  if (splitting) S->merges.reserve(tasks.size());
   for (const RowTask& t : tasks) {
+    if (!splitting) {   // one item per task, its whole visible range
+      if (t.key_lo > t.key_hi)
+        emit(t, 0, 0, 0, -1);
+      else
+        emit(t, t.key_lo, t.key_hi + 1, t.tile_begin, -1);
+      continue;
+    }
     if (t.key_lo > t.key_hi) {  // nothing visible (only with a key-range option)
       emit(t, 0, 0, 0, -1);
       continue;
@@ -590,7 +619,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
       const int64_t step = chunk_tiles * NK;
       int64_t c = a;
       while (c < e) {
-        const int64_t nxt = std::min<int64_t>((c / NK * NK) + step, e);
+        const int64_t nxt = std::min<int64_t>(((c >> nk_sh) << nk_sh) + step, e);
         chunks.emplace_back((int32_t)c, (int32_t)nxt);
         c = nxt;
       }
@@ -598,7 +627,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (o.num_kv_chunks > 0) {
       const int64_t L = S->reqs[t.b].kv_len;
       int64_t clen = (L + o.num_kv_chunks - 1) / o.num_kv_chunks;
-      clen = std::max<int64_t>(NK, (clen + NK - 1) / NK * NK);
+      clen = std::max<int64_t>(NK, ((clen + NK - 1) >> nk_sh) << nk_sh);
       for (int64_t c0 = 0; c0 < L; c0 += clen)
         add(std::max<int64_t>(c0, t.key_lo), std::min<int64_t>(c0 + clen, (int64_t)t.key_hi + 1));
     } else {
@@ -618,7 +647,7 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
     m.pad0 = m.pad1 = 0;
     S->merges.push_back(m);
     for (const auto& c : chunks) {
-      const int32_t tb = std::max(t.tile_begin, c.first / NK * NK);
+      const int32_t tb = std::max(t.tile_begin, (c.first >> nk_sh) << nk_sh);
       emit(t, c.first, c.second, tb, slots++);
     }
   }
