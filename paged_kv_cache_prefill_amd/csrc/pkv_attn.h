@@ -72,7 +72,26 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
-  const WorkItem it = a.work[blockIdx.x];
+  // The first dyn_base work groups (one per concurrent slot, all started at
+  // once) take their own task; later ones, which start as slots free up, take
+  // the next task of the longest-first list, whichever XCD they run on, so an
+  // XCD that runs slower ends up with shorter tasks.  Each later group takes
+  // exactly one index, so the one that gets the last index knows every other
+  // group of this launch has taken its own and can put the counter back.
+  // (short tiles only: the prefill tile's launches with more tasks than slots
+  // are grouped by XCD, and its register budget has no room for this)
+  int widx = blockIdx.x;
+  if (WN > 1 && a.dyn_base > 0 && widx >= a.dyn_base) {
+    __shared__ int lds_task;
+    if (threadIdx.x == 0) {
+      const int v = atomicAdd(a.dyn_next, 1);
+      if (v == a.num_work - a.dyn_base - 1) atomicExch(a.dyn_next, 0);
+      lds_task = a.dyn_base + v;
+    }
+    __syncthreads();
+    widx = __builtin_amdgcn_readfirstlane(lds_task);
+  }
+  const WorkItem it = a.work[widx];
   if (it.nrows == 0) return;                    // padding task (whole work group)
   const ReqInfo rq = a.reqs[it.b];
   const int G = a.group;

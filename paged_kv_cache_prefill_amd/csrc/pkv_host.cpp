@@ -72,7 +72,8 @@ struct Schedule {
   std::vector<WorkItem> work;
   std::vector<MergeItem> merges;
   // int workspace layout
-  size_t off_reqs = 0, off_work = 0, off_merge = 0, off_pages = 0, int_bytes = 0;
+  size_t off_reqs = 0, off_work = 0, off_merge = 0, off_dyn = 0, off_pages = 0, int_bytes = 0;
+  int32_t dyn_base = 0;   // > 0: tasks from here on are taken in work-group start order
   size_t off_mask = 0, mask_bytes = 0;   // custom mask bits (0 bytes: none)
   // float workspace layout
   size_t off_part_lse = 0, float_bytes = 0;
@@ -263,7 +264,8 @@ int64_t choose_chunk_tiles(const std::vector<int64_t>& pieces, int64_t slots, in
 constexpr int kNumXcds = 8;
 
 
-void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_t>& costs,
+// Returns true when it grouped tasks by XCD (the order must then stay fixed).
+bool order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_t>& costs,
                     int32_t batch, int32_t hkv, std::vector<WorkItem>* work) {
   SchedScratch& T = g_scr;
   const size_t n = items.size();
@@ -276,6 +278,7 @@ void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_
   auto longest_first = [&] {
     work->resize(n);
     for (size_t i = 0; i < n; ++i) (*work)[T.start[max_cost - costs[i]]++] = items[i];
+    return false;
   };
   // Reuse exists only when a group has several query tiles (chunks of one
   // tile read disjoint keys).  Tasks of one tile are emitted consecutively.
@@ -332,6 +335,7 @@ void order_for_xcds(const std::vector<WorkItem>& items, const std::vector<int32_
     const int x = T.gxcd[T.gid[i]];
     (*work)[next[x]++ * kNumXcds + x] = items[i];
   }
+  return true;
 }
 
 // Smallest and largest page id (the plan scans every page-table entry; the
@@ -654,7 +658,12 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   S->num_slots = slots;
   if (items.size() > (size_t)INT32_MAX / 2)
     return fail(PKV_EINVAL, "batch too large: %zu tasks", items.size());
-  order_for_xcds(items, costs, batch, hkv, &S->work);
+  const bool grouped = order_for_xcds(items, costs, batch, hkv, &S->work);
+  // short tiles (one work group per CU): when the list is plain longest-first
+  // and longer than one work group per CU, the tasks beyond the first round
+  // are taken in the order their work groups start
+  S->dyn_base = (kind != TILE_PREFILL && !grouped && (int64_t)S->work.size() > kNumCUs)
+                    ? kNumCUs : 0;
 
   // ---- workspace layouts
   size_t off = 0;
@@ -664,6 +673,8 @@ pkv_status schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
   off = align_up(off + S->work.size() * sizeof(WorkItem), 256);
   S->off_merge = off;
   off = align_up(off + S->merges.size() * sizeof(MergeItem), 256);
+  S->off_dyn = off;   // the start-order task counter, uploaded as zero
+  off = align_up(off + sizeof(int32_t), 256);
   S->off_pages = off;
   off = align_up(off + (size_t)S->num_indices * sizeof(int32_t), 256);
   S->off_mask = off;
@@ -1094,6 +1105,8 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   a.part_lse = p->float_ws ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p->float_ws) +
                                                       S.off_part_lse)
                            : nullptr;
+  a.dyn_base = S.dyn_base;
+  a.dyn_next = reinterpret_cast<int32_t*>(p->int_ws + S.off_dyn);
   a.q_s_tok = q_s_tok;
   a.q_s_head = q_s_head;
   a.k_s_page = (uint32_t)k_s_page;

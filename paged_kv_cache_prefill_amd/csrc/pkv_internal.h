@@ -103,6 +103,11 @@ struct AttnArgs {
   // gather check only: [sum kv_len, Hkv, D] outputs of the K and V tiles as loaded
   void* gather_k;
   void* gather_v;
+  // dyn_base > 0: work groups dyn_base.. take tasks dyn_base.. in the order
+  // they start, from the counter dyn_next (zero between launches: the group
+  // that takes the last task puts it back)
+  int32_t dyn_base;
+  int32_t* dyn_next;
 };
 
 struct SplitMergeArgs {
