@@ -193,6 +193,10 @@ pkv_status pkv_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
  * Shapes are checked against the plan: heads, head_dim (q, k, v separately),
  * page_size and dtype must match; q_rows, o_rows and lse_rows are minimums
  * (callers pad); every referenced page id must be below k_pages and v_pages.
+ * A run uses its plan's workspaces (fp32 partials of split query tiles in
+ * float_ws; in int_ws a task counter that is back at zero when the launch
+ * ends), so runs of one plan must not overlap (one stream, or synchronised
+ * streams); runs of different plans may.
  */
 pkv_status pkv_run(pkv_plan_t plan,
                    const void* q, int64_t q_rows, int32_t q_heads, int32_t q_dim,
