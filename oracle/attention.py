@@ -345,8 +345,9 @@ def attention_rows(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_page_indices,
                    custom_mask=None, mask_indptr=None, logits_soft_cap=0.0):
     """``attention`` restricted to some rows and q heads of request b.
 
-    Same definition, float64; used to check full-size workloads on sampled
-    outputs.  rows are request-local query indices, heads q-head indices.
+    Same definition, float64, for a subset of the outputs (pinned against
+    ``attention`` on every row).  rows are request-local query indices, heads
+    q-head indices.
     Returns o [len(rows), len(heads), D] and lse [len(rows), len(heads)].
     The request's keys are read page by page through its page table.
     """

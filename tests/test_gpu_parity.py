@@ -189,7 +189,7 @@ def test_empty_batch(pk):
 
 
 # ---------------------------------------------------------------------------
-# config 2: paged batch prefill (full size, sampled outputs)
+# config 2: paged batch prefill (full size, every output element)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("window_left", [-1, 127])
 def test_config2_paged_prefill(pk, window_left):

@@ -1,7 +1,7 @@
 """Tree-draft verify (custom topology masks) on the GPU against the oracle:
 tiny exhaustive cases over page sizes, head dims, dtypes, windows and both
 tile shapes; arbitrary (non-tree) masks with fully masked rows; full-size
-batches on sampled rows; reductions to the causal path."""
+batches with every output element compared; reductions to the causal path."""
 import zlib
 
 import numpy as np
