@@ -688,7 +688,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   if constexpr (kQL) {
     // Q rows first (row rr of the task: packed row row0 + rr, rows past the
     // task re-read its last row), then K0, V0 and K1 before the first wait,
-    // which leaves K1 in flight.  SGPR base: the task's first position; lane
+    // which leaves V0 and K1 in flight.  SGPR base: the task's first position; lane
     // offsets: (position - first) * s_tok + head * s_head + chunk, in bytes.
     // LDS slot c of row rr holds chunk c ^ (rr % 8) (rows are a multiple of
     // the bank width apart: the fragment reads below would otherwise take
@@ -719,7 +719,10 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
         issue_part(Flag<true>{}, tb + NWG, lds_k1);
       }
     }
-    if (ntiles > 1) wait_vm_lgkm0<NI>(); else wait_vm_lgkm0<0>();
+    // Q and K0 landed; V0 (and K1) may still be in flight: the first tile's
+    // score products need only Q and K0, and the first step's wait before its
+    // PV products covers V0 (in-order completion)
+    if (ntiles > 1) wait_vm_lgkm0<2 * NI>(); else if (ntiles == 1) wait_vm_lgkm0<NI>(); else wait_vm_lgkm0<0>();
     __syncthreads();
 #pragma unroll
     for (int qb = 0; qb < (kDump ? 0 : QB); ++qb) {
