@@ -399,6 +399,11 @@ def coverage_cases():
     fp8 = {"kv_dtype": "fp8_e4m3", "k_scale": 0.5, "v_scale": 2.0}
     cases.append(("verify_b64_hkv8_fp8kv", W.config4(batch=64, values=False), fp8))
     cases.append(("paged_prefill_b8_fp8kv", W.config2(values=False), fp8))
+    # FP8 caches under a topology mask, and under a soft-cap
+    cases.append(("tree_verify_b16_hkv8_8nodes_fp8kv", W.tree_verify(batch=16, values=False), fp8))
+    capped8 = W.config2(values=False)
+    capped8.logits_soft_cap = 50.0
+    cases.append(("paged_prefill_b8_softcap50_fp8kv", capped8, fp8))
     for ql in (1, 64):
         for wl in (-1, 4095):
             cases.append((f"long_ctx_q{ql}_w{wl}_8chunks",
