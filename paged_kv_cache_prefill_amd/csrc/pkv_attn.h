@@ -789,15 +789,15 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   const bool to_partial = it.slot >= 0;
 
   if constexpr (WN == 1) {
+    if (to_partial) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int rl = wm * MW + qb * 16 + l16;  // row within the task
-      const int r = it.row0 + rl;
-      if (rl >= it.nrows || r >= R) continue;
-      float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
-      if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
-      const float lse2 = l_tot[qb] > 0.f ? m_run[qb] + fast_log2(l_tot[qb]) : kNegInf;
-      if (to_partial) {
+      for (int qb = 0; qb < QB; ++qb) {
+        const int rl = wm * MW + qb * 16 + l16;  // row within the task
+        const int r = it.row0 + rl;
+        if (rl >= it.nrows || r >= R) continue;
+        float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+        if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
+        const float lse2 = l_tot[qb] > 0.f ? m_run[qb] + fast_log2(l_tot[qb]) : kNegInf;
         float* dst = a.part_o + ((int64_t)it.slot * (WM * MW) + rl) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -805,19 +805,60 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
           *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = v;
         }
         if (g == 0) a.part_lse[(int64_t)it.slot * (WM * MW) + rl] = lse2;
-      } else {
-        const int pos = r / G;
-        const int h = it.kvh * G + (r - pos * G);
-        const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
-        T* dst = op + orow * D;
+      }
+    } else {
+      // O in the q dtype, staged through LDS (the K/V buffers are free once
+      // the key loop has ended).  A lane holds 4-element pieces of 16 rows, so
+      // storing from registers writes 32-byte pieces of 16 rows per
+      // instruction; from LDS each lane stores a whole 16-byte chunk and one
+      // instruction covers 64 / CH consecutive rows (whole output rows of
+      // consecutive heads).  Wave w's region: its MW rows of CH chunks, chunk
+      // c of row r at position swz_k(r, c); orow_w[r] is row r's output row,
+      // or -1 past the task.  Each wave reads back only what its own lanes
+      // wrote, and LDS completes one wave's accesses in order.
+      static_assert((WM / 2) * MW * D * (int)sizeof(T) <= (int)sizeof(lds_k0), "LDS too small");
+      static_assert(WM * MW * 8 <= (int)sizeof(lds_k1), "LDS too small");
+      char* stage = reinterpret_cast<char*>(wm < WM / 2 ? lds_k0 : lds_v0) +
+                    (wm % (WM / 2)) * MW * D * (int)sizeof(T);
+      int64_t* orow_w = reinterpret_cast<int64_t*>(lds_k1) + wm * MW;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int rw = qb * 16 + l16;           // row within the wave
+        const int rl = wm * MW + rw;            // row within the task
+        const int r = it.row0 + rl;
+        const bool valid = rl < it.nrows && r < R;
+        float inv = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+        if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
+        int64_t orow = -1;
+        if (valid) {
+          const int pos = r / G;
+          const int h = it.kvh * G + (r - pos * G);
+          orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+        }
+        if (g == 0) {
+          orow_w[rw] = orow;
+          if (valid && a.lse != nullptr)
+            a.lse[orow] = l_tot[qb] > 0.f ? (m_run[qb] + fast_log2(l_tot[qb])) * kLn2 : kNegInf;
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           T o4[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(oacc[db][qb][i] * inv);
-          *reinterpret_cast<uint2*>(dst + db * 16 + 4 * g) = *reinterpret_cast<uint2*>(o4);
+          const int c = db * 2 + (g >> 1);      // chunk of elements db * 16 + 4g .. + 3
+          *reinterpret_cast<uint2*>(stage + (rw * CH + swz_k<CH>(rw, c)) * 16 + (g & 1) * 8) =
+              *reinterpret_cast<uint2*>(o4);
         }
-        if (g == 0 && a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = lane; i < MW * CH; i += 64) {
+        const int rw = i / CH, c = i % CH;
+        const int64_t orow = orow_w[rw];
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + (rw * CH + swz_k<CH>(rw, c)) * 16);
+        if (orow >= 0) *reinterpret_cast<uint4*>(op + orow * D + c * 8) = v;
       }
     }
   } else {
