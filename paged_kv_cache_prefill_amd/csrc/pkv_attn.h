@@ -875,7 +875,9 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     float* red_m = reinterpret_cast<float*>(lds_v0);     // [WN][MW]
     float* red_l = red_m + WN * MW;                      // [WN][MW]
     static_assert(WN % 2 == 0 && (WN / 2) * MW * D * 4 <= (int)sizeof(lds_k0), "LDS too small");
-    static_assert(2 * WN * MW * 4 <= (int)sizeof(lds_v0), "LDS too small");
+    // orow_t[r]: output row of row r (any value >= 0 for a partial tile), -1 past the task
+    int64_t* orow_t = reinterpret_cast<int64_t*>(red_l + WN * MW);
+    static_assert(2 * WN * MW * 4 + MW * 8 <= (int)sizeof(lds_v0), "LDS too small");
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (g == 0) {
@@ -884,6 +886,10 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+    // Each wave folds the whole row normalisation into its own slice,
+    // o_w 2^(m_w - mt) / lt with mt = max_w m_w and lt = sum_w l_w 2^(m_w - mt),
+    // so the slices only need adding up; wave 0 writes each row's lse and
+    // output row.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int rl = qb * 16 + l16;
@@ -891,47 +897,53 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < WN; ++w) mt = fmaxf(mt, red_m[w * MW + rl]);
       const float mu = (mt == kNegInf) ? 0.f : mt;
-      const float sc = fast_exp2(m_run[qb] - mu);
+      float lt = 0.f;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) lt += red_l[w * MW + rl] * fast_exp2(red_m[w * MW + rl] - mu);
+      float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
+      const float sc = fast_exp2(m_run[qb] - mu) * inv;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 v = oacc[db][qb] * sc;
         *reinterpret_cast<f32x4*>(red_o_of(wn) + rl * D + ((db * 4 + g) ^ (rl & 7)) * 4) = v;
       }
+      if (wn == 0 && g == 0) {
+        const int r = it.row0 + rl;
+        const float lse2 = lt > 0.f ? mt + fast_log2(lt) : kNegInf;
+        int64_t orow = -1;
+        if (rl < it.nrows && r < R) {
+          if (to_partial) {
+            orow = 0;
+            a.part_lse[(int64_t)it.slot * MW + rl] = lse2;
+          } else {
+            const int pos = r / G;
+            const int h = it.kvh * G + (r - pos * G);
+            orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
+            if (a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+          }
+        }
+        orow_t[rl] = orow;
+      }
     }
     __syncthreads();
-    // Every thread finishes 4 consecutive head-dim elements of some rows.
+    // Every thread adds up the slices for 4 consecutive head-dim elements of some rows.
     for (int idx = tid; idx < MW * (D / 4); idx += 64 * NWAVE) {
       const int rl = idx / (D / 4);
       const int d4 = idx - rl * (D / 4);
-      float mt = kNegInf;
-#pragma unroll
-      for (int w = 0; w < WN; ++w) mt = fmaxf(mt, red_m[w * MW + rl]);
-      const float mu = (mt == kNegInf) ? 0.f : mt;
-      float lt = 0.f;
+      const int64_t orow = orow_t[rl];
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < WN; ++w) {
-        lt += red_l[w * MW + rl] * fast_exp2(red_m[w * MW + rl] - mu);
+      for (int w = 0; w < WN; ++w)
         acc += *reinterpret_cast<const f32x4*>(red_o_of(w) + rl * D + (d4 ^ (rl & 7)) * 4);
-      }
-      const int r = it.row0 + rl;
-      if (rl >= it.nrows || r >= R) continue;
-      float inv = lt > 0.f ? 1.f / lt : 0.f;
-      if constexpr (kFp8) inv *= a.v_scale;   // V = codes * v_scale
-      const float lse2 = lt > 0.f ? mt + fast_log2(lt) : kNegInf;
+      if (orow < 0) continue;
       if (to_partial) {
-        float* dst = a.part_o + ((int64_t)it.slot * MW + rl) * D + d4 * 4;
-        *reinterpret_cast<f32x4*>(dst) = acc * inv;
-        if (d4 == 0) a.part_lse[(int64_t)it.slot * MW + rl] = lse2;
+        *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)it.slot * MW + rl) * D + d4 * 4) = acc;
       } else {
-        const int pos = r / G;
-        const int h = it.kvh * G + (r - pos * G);
-        const int64_t orow = (int64_t)(rq.qo_start + pos) * a.num_qo_heads + h;
         T o4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i] * inv);
+        for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[i]);
         *reinterpret_cast<uint2*>(op + orow * D + d4 * 4) = *reinterpret_cast<uint2*>(o4);
-        if (d4 == 0 && a.lse != nullptr) a.lse[orow] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
       }
     }
   }
