@@ -370,6 +370,39 @@ def test_split_tiles_merged_in_every_run(pk, case):
         check_full(w, o.float().cpu().numpy(), lse.cpu().numpy(), f"{case} run {run_i}")
 
 
+@pytest.mark.parametrize("window_left", [-1, 4095])
+def test_million_key_context(pk, window_left):
+    """One request with 2^20 + 37 keys (65,539 pages of 16 in a permuted pool
+    1.5 times that size, ragged last page) and 4 query rows, Hq 8 / Hkv 1,
+    D 64: key positions, page ids and page-table offsets far beyond those of
+    the benchmark configurations, split into chunks and merged; every output
+    element against the oracle, with NaN in every slot the request does not
+    reference."""
+    w = W.build("million", [4], [(1 << 20) + 37], 8, 1, 64, 16, True, window_left, W.BF16,
+                seed=41, poison=True)
+    o, lse, p = run(pk, w)
+    if window_left < 0:
+        assert p.info["num_merge_items"] > 0
+    check_full(w, o, lse, f"million keys, window {window_left}")
+
+
+@pytest.mark.parametrize("causal,window_left", [(True, 40), (False, -1)])
+def test_thousands_of_requests(pk, causal, window_left):
+    """2,500 requests of 1-6 query rows over 1-300 keys each on 7-key pages
+    (the general page path: a page-table lookup per key with a divisor that
+    is not a power of two), Hq 8 / Hkv 2, D 64, fp16: a task list of
+    thousands of work groups, most of them taken in the order their groups
+    start; every output element against the oracle over NaN-poisoned pools."""
+    rng = np.random.default_rng(43)
+    qo = rng.integers(1, 7, size=2500)
+    kv = qo + rng.integers(0, 295, size=2500)
+    w = W.build("many", qo, kv, 8, 2, 64, 7, causal, window_left, W.FP16, seed=None, rng=rng,
+                poison=True)
+    o, lse, p = run(pk, w)
+    assert p.info["num_work_items"] >= 5000
+    check_full(w, o, lse, f"2500 requests causal={causal} window={window_left}")
+
+
 def test_key_range_partial_state(pk):
     w = W.build("range", [6, 40], [100, 70], 4, 2, 128, 16, True, 10, W.BF16, seed=16)
     for a, e in ((0, 30), (30, 64), (64, 101), (90, 95)):
