@@ -323,29 +323,48 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
     const int jl = j0 + wn * NW + 4 * g;
     // logits soft-cap: scores become cap * log2(e) * tanh(sm_scale * s / cap),
     // already in log2 units; masked scores are set to -inf after this, below.
-    // tanh(y) is 1 - 2 / (1 + e^{2y}) (exp2 and a reciprocal) for |y| >= 1/4
-    // and its Taylor series y (1 - y^2/3 + 2y^4/15 - 17y^6/315) below, where
-    // the first form would lose the small value to cancellation (relative
-    // error of either below 1e-6, so a large cap reproduces the plain logit).
+    // tanh(y) = 1 - 2 / (1 + e^{2y}) (exp2 and a reciprocal) is within a few
+    // ulp of 1 of tanh, so the capped logit is within ~2e-7 * cap of its
+    // value: caps up to 1024 use this form alone.  Larger caps (cap_series)
+    // would turn that into a visible error for logits far below the cap, so
+    // there |y| < 1/4 takes the Taylor series y (1 - y^2/3 + 2y^4/15 -
+    // 17y^6/315) instead, where the first form would lose the small value to
+    // cancellation (relative error of either below 1e-6, so a huge cap
+    // reproduces the plain logit).
     const float mul = kCap ? 1.f : a.scale_log2;
     if constexpr (kCap) {
+      if (a.cap_series) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+          for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float y = s[kb][qb][i] * a.cap_in;
-            const float y2 = y * y;
-            const float series =
-                y * __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2, -17.f / 315.f,
-                                                                         2.f / 15.f),
-                                                      -1.f / 3.f),
-                                   1.f);
-            const float e = fast_exp2(y * 2.8853900817779268f);   // e^{2y}
-            const float big = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
-            s[kb][qb][i] = (fabsf(y) < 0.25f ? series : big) * a.cap_out;
-          }
+            for (int i = 0; i < 4; ++i) {
+              const float y = s[kb][qb][i] * a.cap_in;
+              const float y2 = y * y;
+              const float series =
+                  y * __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2, -17.f / 315.f,
+                                                                           2.f / 15.f),
+                                                        -1.f / 3.f),
+                                     1.f);
+              const float e = fast_exp2(y * 2.8853900817779268f);   // e^{2y}
+              const float big = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
+              s[kb][qb][i] = (fabsf(y) < 0.25f ? series : big) * a.cap_out;
+            }
+      } else {
+        // 2 log2(e) * cap_in folded into one multiplier
+        const float c2 = a.cap_in * 2.8853900817779268f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e = fast_exp2(s[kb][qb][i] * c2);   // e^{2y}
+              s[kb][qb][i] =
+                  __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f) * a.cap_out;
+            }
+      }
     }
     // Lazy rescaling: exponents are taken against a reference m_run per row
     // that moves only when a score exceeds it by more than kTau (log2 units),

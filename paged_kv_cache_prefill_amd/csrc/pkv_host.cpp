@@ -1128,6 +1128,7 @@ pkv_status pkv_run(pkv_plan_t p, const void* q, int64_t q_rows, int32_t q_heads,
   // the kernel's raw score is q . codes; the logit is sm_scale * k_scale times it
   a.cap_in = p->soft_cap > 0.f ? p->sm_scale * (p->kv_fp8 ? p->k_scale : 1.f) / p->soft_cap : 0.f;
   a.cap_out = p->soft_cap > 0.f ? p->soft_cap * 1.4426950408889634f : 0.f;
+  a.cap_series = p->soft_cap > 1024.f ? 1 : 0;
   hipError_t e = launch_attention(S.tile_kind, (int)p->dtype, S.head_dim, a, hs);
   if (e != hipSuccess) return fail(PKV_EHIP, "attention launch: %s", hipGetErrorString(e));
   if (!S.merges.empty()) {

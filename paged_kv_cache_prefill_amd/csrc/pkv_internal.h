@@ -98,6 +98,7 @@ struct AttnArgs {
   // = cap * log2(e) * tanh(sm_scale * raw / cap); cap_out = 0: no cap
   float cap_in;            // sm_scale / cap
   float cap_out;           // cap * log2(e)
+  int32_t cap_series;      // 1: caps above 1024, tanh through its Taylor series near 0
   int32_t kv_fp8;          // 1: K/V are FP8 E4M3 codes (k_scale folded into scale_log2)
   float v_scale;           // FP8 V: value = code * v_scale
   // gather check only: [sum kv_len, Hkv, D] outputs of the K and V tiles as loaded

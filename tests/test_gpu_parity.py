@@ -537,6 +537,24 @@ def test_soft_cap_tiny(pk, cap, d, dtype):
                          f"cap={cap} d={d} causal={causal} w={wl} tile={tile}")
 
 
+@pytest.mark.parametrize("cap", [1000.0, 1024.0, 1025.0, 4096.0])
+def test_soft_cap_small_logits_both_forms(pk, cap):
+    """Logits far below the cap (sm_scale 0.01: |s| ~ 0.1, s / cap ~ 1e-4),
+    where tanh(y) = 1 - 2 / (1 + e^{2y}) loses most of y to cancellation:
+    caps up to 1024 take that form alone (its error, a few ulp of 1 times
+    the cap, stays far inside the tolerances), larger ones its Taylor series
+    near 0.  Both on both tile shapes, against the oracle."""
+    rng = np.random.default_rng(int(cap))
+    w = W.build("capsmall", [1, 17, 40], [30, 17, 200], 8, 2, 128, 16, True, -1, W.BF16,
+                seed=int(rng.integers(1 << 30)), poison=True, sm_scale=0.01)
+    w.logits_soft_cap = cap
+    ref_o, ref_lse = oracle_full(w)
+    tensors = device_inputs(w)
+    for tile in (1, 2):
+        o, lse, _ = run(pk, w, tensors, tile=tile)
+        assert_close(o, lse, ref_o, ref_lse, W.BF16, f"cap={cap} tile={tile}")
+
+
 def test_soft_cap_full_size(pk):
     w = W.config2(poison=True)
     w.logits_soft_cap = 5.0
