@@ -490,6 +490,31 @@ def test_run_refuses_mismatches(pk):
     assert torch.equal(l_pad[:q.shape[0]], l_ref) and torch.all(l_pad[q.shape[0]:] == 5)
 
 
+def test_two_plans_on_two_streams(pk):
+    """Runs of different plans may overlap: a verify batch (tasks past the
+    first 256 taken in start order from its own counter) and a split-KV
+    prefill (merged by its own merge launch), each run five times on its own
+    stream with no synchronisation between the two streams, both checked in
+    full against the oracle."""
+    w1 = W.config4(batch=64, num_kv_heads=8, poison=True)
+    w2 = W.build("two_streams", [40, 3, 70], [3000, 900, 2500], 16, 4, 128, 16, True, -1,
+                 W.BF16, seed=51, poison=True)
+    p1 = plan_for(pk, w1)
+    p2 = plan_for(pk, w2, num_kv_chunks=3)
+    assert p1.info["num_work_items"] > 256 and p2.info["num_merge_items"] > 0
+    t1, t2 = device_inputs(w1), device_inputs(w2)
+    torch.cuda.synchronize()    # plans uploaded on the current stream
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(5):
+        with torch.cuda.stream(s1):
+            o1, l1 = p1.run(*t1)
+        with torch.cuda.stream(s2):
+            o2, l2 = p2.run(*t2)
+    torch.cuda.synchronize()
+    check_full(w1, o1.float().cpu().numpy(), l1.cpu().numpy(), "verify on stream 1")
+    check_full(w2, o2.float().cpu().numpy(), l2.cpu().numpy(), "split prefill on stream 2")
+
+
 def test_plan_refused_under_stream_capture(pk):
     """plan uploads its task list from a staging buffer whose reuse is ordered by
     an event, which capture would never record: a runnable plan on a capturing
