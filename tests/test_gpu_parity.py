@@ -199,6 +199,25 @@ def test_config2_paged_prefill(pk, window_left):
     check_full(w, o, lse, f"config2 w={window_left}")
 
 
+@pytest.mark.parametrize("d,page,dtype", [(64, 48, W.FP16), (128, 2, W.BF16)])
+@pytest.mark.parametrize("window_left", [-1, 127])
+def test_paged_batch_other_page_paths(pk, d, page, dtype, window_left):
+    """The paged batch's lengths (8 requests, qo 128-1024, kv = qo + 0-2048,
+    Hq 32 / Hkv 8, causal) on the prefill tile's two other page-address
+    paths, at full size: 48-key pages (any page size: a page-table lookup
+    per key row and a multiply-shift division) and 2-key pages (power-of-two
+    pages shorter than one load instruction's rows: a fixed slot per lane);
+    every output element against the oracle over NaN-poisoned pools."""
+    rng = np.random.default_rng(2000 + d + page)
+    qo = rng.integers(128, 1024, size=8, endpoint=True)
+    kv = qo + rng.integers(0, 2048, size=8, endpoint=True)
+    w = W.build("paged_batch_pages", qo, kv, 32, 8, d, page, True, window_left, dtype,
+                seed=None, rng=rng, poison=True)
+    o, lse, p = run(pk, w)
+    assert p.info["tile_rows"] == 128
+    check_full(w, o, lse, f"paged batch d={d} page={page} window={window_left}")
+
+
 # ---------------------------------------------------------------------------
 # config 3: non-causal sliding window, page 1024 and 16
 # ---------------------------------------------------------------------------
