@@ -218,6 +218,23 @@ def test_paged_batch_other_page_paths(pk, d, page, dtype, window_left):
     check_full(w, o, lse, f"paged batch d={d} page={page} window={window_left}")
 
 
+@pytest.mark.parametrize("d,page,dtype", [(64, 48, W.FP16), (128, 2, W.BF16)])
+def test_verify_other_page_paths(pk, d, page, dtype):
+    """Verify batch 16 / Hkv 8 (4 queries per request, kv 512-8192, causal)
+    on the short-query tile's other page paths, at full size: 48-key pages
+    (a page-table lookup per key row) and 2-key pages (a fixed slot per
+    lane), where Q is loaded into registers instead of through LDS and the
+    split chunks are merged; every output element against the oracle over
+    NaN-poisoned pools."""
+    rng = np.random.default_rng(4000 + d + page)
+    kv = rng.integers(512, 8192, size=16, endpoint=True)
+    w = W.build("verify_pages", [4] * 16, kv, 32, 8, d, page, True, -1, dtype, seed=None,
+                rng=rng, poison=True)
+    o, lse, p = run(pk, w)
+    assert p.info["tile_rows"] == 16 and p.info["num_merge_items"] > 0
+    check_full(w, o, lse, f"verify d={d} page={page}")
+
+
 # ---------------------------------------------------------------------------
 # config 3: non-causal sliding window, page 1024 and 16
 # ---------------------------------------------------------------------------
