@@ -352,8 +352,10 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
               s[kb][qb][i] = (fabsf(y) < 0.25f ? series : big) * a.cap_out;
             }
       } else {
-        // 2 log2(e) * cap_in folded into one multiplier
+        // 2 log2(e) * cap_in folded into one multiplier, and cap_out * (1 - 2r)
+        // into one fused multiply-add
         const float c2 = a.cap_in * 2.8853900817779268f;
+        const float m2 = -2.f * a.cap_out;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -361,8 +363,7 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float e = fast_exp2(s[kb][qb][i] * c2);   // e^{2y}
-              s[kb][qb][i] =
-                  __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f) * a.cap_out;
+              s[kb][qb][i] = __builtin_fmaf(m2, __builtin_amdgcn_rcpf(1.f + e), a.cap_out);
             }
       }
     }
