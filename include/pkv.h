@@ -354,10 +354,14 @@ pkv_status pkv_plan_get_info(pkv_plan_t plan, pkv_plan_info* info);
 
 /*
  * Copy the plan's task list to host memory as int32 records of 8 fields:
- * {request, kv_head, row0, num_rows, kv_begin, kv_end, partial_slot, 0}
- * (rows are packed (position, head-in-group) rows of that kv head; a
- * partial_slot >= 0 marks one chunk of a split query tile).  Writes at most
- * `capacity` records and stores the total count in *count.  Host-only.
+ * {request, kv_head, row0, num_rows, kv_begin, kv_end, partial_slot, tile_begin}
+ * in launch order (record i is work group i).  Rows are packed (position,
+ * head-in-group) rows of that kv head; the task loads key tiles from
+ * tile_begin (<= kv_begin, on the request's key-tile grid) up to kv_end and
+ * masks keys below kv_begin; a partial_slot >= 0 marks one chunk of a split
+ * query tile.  Lists grouped by XCD are padded with empty records
+ * (num_rows 0, partial_slot -1).  Writes at most `capacity` records and
+ * stores the total count in *count.  Host-only.
  */
 pkv_status pkv_plan_get_work(pkv_plan_t plan, int32_t* out, int64_t capacity,
                              int64_t* count);
