@@ -26,8 +26,10 @@
 //     accumulation.  In that orientation each lane owns one query row (lane %
 //     16) in every MFMA result, so the row statistics stay per lane and the P
 //     fragment produced by the first MFMA is directly the B operand of the
-//     second (no shuffles); row max is reduced across the 4 lane groups with
-//     two xor-shuffles, the row sum only once at the end.
+//     second (no shuffles).  The exponentials are taken against a per-row
+//     reference that moves only when a score exceeds it by more than 2^8
+//     (lazy rescaling): then, and only then, the row max is reduced across
+//     the 4 lane groups with two xor-shuffles; the row sum once at the end.
 //   * Softmax runs in the log2 domain (scale * log2 e folded into one
 //     multiply, hardware exp2); lse is converted to natural log on output.
 //   * Tiles entirely inside every row's visible band skip the mask; tiles
