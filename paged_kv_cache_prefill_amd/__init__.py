@@ -172,7 +172,7 @@ def _ptr_i32(a):
 
 def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0, custom_mask=None,
              mask_indptr=None, logits_soft_cap=0.0, kv_dtype=None, k_scale=1.0, v_scale=1.0,
-             split_tiles=0):
+             split_tiles=0, batch=None):
     o = _PlanOptions()
     o.num_kv_chunks, o.kv_begin, o.kv_end, o.tile = int(num_kv_chunks), int(kv_begin), \
         int(kv_end), int(tile)
@@ -188,7 +188,19 @@ def _options(num_kv_chunks=0, kv_begin=0, kv_end=-1, tile=0, custom_mask=None,
             raise PkvError(PKV_EINVAL, "custom_mask and mask_indptr: expected both or neither")
         m = np.ascontiguousarray(np.asarray(custom_mask).reshape(-1), dtype=np.uint8)
         ind = np.ascontiguousarray(np.asarray(mask_indptr).reshape(-1), dtype=np.int64)
-        o.custom_mask = m.ctypes.data if m.size else None
+        if batch is not None:
+            # the library reads mask_indptr[0..batch] and custom_mask[0, mask_indptr[batch])
+            if len(ind) != batch + 1:
+                raise PkvError(PKV_EINVAL, f"mask_indptr: expected {batch + 1} entries, "
+                                           f"given {len(ind)}")
+            if int(ind[-1]) > m.size:
+                raise PkvError(PKV_EINVAL, f"custom_mask: expected at least mask_indptr[{batch}]"
+                                           f" = {int(ind[-1])} bytes, given {m.size}")
+        if m.size == 0:
+            # a mask of no bytes (every request has no row or no key) still
+            # names its storage: NULL would mean "no mask"
+            m = np.zeros(1, dtype=np.uint8)
+        o.custom_mask = m.ctypes.data
         o.mask_indptr = ind.ctypes.data
         o._keep = (m, ind)   # the arrays must outlive the call
     return o
@@ -365,7 +377,7 @@ def _make_plan(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_h
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(head_dim)
     code = _dtype_code(dtype)
-    o = _options(**opts)
+    o = _options(**opts, batch=batch)
     args = (_ptr_i32(qo), _ptr_i32(kv), _ptr_i32(idx), len(idx), _ptr_i32(last), batch,
             int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
             int(bool(causal)), int(window_left))

@@ -277,6 +277,16 @@ def test_custom_mask_refusals_and_plan():
     bad0[0] = -1
     with pytest.raises(pk.PkvError, match="mask_indptr"):
         pk.plan_host(**base, custom_mask=data, mask_indptr=bad0)
+    # the binding checks both arrays' lengths before the library reads them
+    with pytest.raises(pk.PkvError, match="mask_indptr: expected 3 entries"):
+        pk.plan_host(**base, custom_mask=data, mask_indptr=ind[:2])
+    with pytest.raises(pk.PkvError, match="custom_mask: expected at least"):
+        pk.plan_host(**base, custom_mask=data[:-1], mask_indptr=ind)
+    # a mask of no bytes (no request has a query row) is a mask, not a missing one
+    e_data, e_ind = W.pack_custom_mask([np.zeros((0, 6), bool), np.zeros((0, 7), bool)])
+    assert len(e_data) == 0
+    p = pk.plan_host(**dict(base, qo_indptr=[0, 0, 0]), custom_mask=e_data, mask_indptr=e_ind)
+    assert p.info["total_q_rows"] == 0
 
 
 def test_sampling_refusals_on_host():
