@@ -303,8 +303,14 @@ class Plan:
             raise PkvError(PKV_ENOTPLANNED, "plan was built host-only; it cannot run")
         if q.dim() != 3:
             raise PkvError(PKV_ELAYOUT, f"q: expected [rows, heads, head_dim], given {q.dim()}-D")
-        if q.stride(2) != 1:
+        if q.numel() == 0:
+            # no query row: strides mean nothing (numpy gives empty arrays zero
+            # strides); hand the library packed ones
+            q_s_tok, q_s_head = q.shape[1] * q.shape[2], q.shape[2]
+        elif q.stride(2) != 1:
             raise PkvError(PKV_ELAYOUT, f"q: head_dim stride must be 1, given {q.stride(2)}")
+        else:
+            q_s_tok, q_s_head = q.stride(0), q.stride(1)
         kv_ok = (torch.uint8, torch.float8_e4m3fn) if self.kv_fp8 else (self.dtype,)
         for name, t, ok in (("q", q, (self.dtype,)), ("paged_k", paged_k, kv_ok),
                             ("paged_v", paged_v, kv_ok)):
@@ -329,7 +335,7 @@ class Plan:
             raise PkvError(PKV_ELAYOUT, "lse: expected a packed fp32 [rows, num_qo_heads] tensor")
         code = _dtype_code(self.dtype)
         _check(_lib.pkv_run(
-            self._h, q.data_ptr(), q.shape[0], q.shape[1], q.shape[2], q.stride(0), q.stride(1),
+            self._h, q.data_ptr(), q.shape[0], q.shape[1], q.shape[2], q_s_tok, q_s_head,
             k.data_ptr(), k.shape[0], k.shape[1], k.shape[2], k.shape[3],
             k.stride(0), k.stride(1), k.stride(2),
             v.data_ptr(), v.shape[0], v.shape[1], v.shape[2], v.shape[3],
