@@ -90,3 +90,14 @@ def test_kernel_source_hash_covers_the_kernel_files():
         with open(path, "rb") as f:
             h.update(f.read())
     assert h.hexdigest() == bench.kernel_source_sha()
+
+
+def test_cpu_baseline_times_whole_passes():
+    """The host baseline runs the oracle over every request of the workload in
+    whole passes until its minimum time, and says how much it ran."""
+    w = W.build("cpu", [3, 5], [20, 9], 4, 2, 64, 4, True, -1, W.BF16, seed=3)
+    r = bench.cpu_baseline(w, min_s=0.2, budget_s=5.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert "whole pass" in r["sample"] and "over all 2 requests" in r["sample"]
+    passes = int(r["sample"].split("oracle, ")[1].split(" whole")[0])
+    assert passes >= 1
