@@ -306,15 +306,17 @@ size_t pkv_chain_speculative_sampling_workspace_size(int32_t batch_size, int32_t
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, rule, kernels and results
  * as pkv_chain_speculative_sampling, minus the workspace: the per-tile sums
- * live in a 4 MiB array the library holds on each GPU it runs on (from the
- * first call on that GPU until the process ends).  Nothing is allocated by
+ * live in a 4 MiB array the library holds on each GPU it runs on (the GPU of
+ * `stream`, the current one for the null stream; from the first call on that
+ * GPU until the process ends).  Nothing is allocated by
  * this call.  Limit: batch * ceil(vocab / 1024) <= 262144 tiles (e.g. batch
  * 256 at a 2^20 vocabulary); larger sizes are refused (PKV_EINVAL) before any
  * device call.  Every call on one GPU shares that array, and each call writes
  * every entry it reads before reading it: calls on one GPU must be ordered
  * (one stream, or synchronised streams) -- calls that overlap on one GPU race.
  * The first call on each GPU looks up the array's device address
- * (hipGetSymbolAddress, with that GPU current): make it outside graph capture.
+ * (hipGetSymbolAddress, with that GPU made current for the lookup and the
+ * caller's current device restored): make it outside graph capture.
  */
 pkv_status pkv_chain_speculative_sampling_no_alloc(const float* draft_probs,
                                                    const int32_t* draft_token_ids,

@@ -1332,7 +1332,7 @@ pkv_status pkv_chain_speculative_sampling_no_alloc(const float* draft_probs,
                 kSpecScratchBytes / 16, kSpecScratchBytes, batch, (vocab_size + 1023) / 1024,
                 need / 16);
   void* ws = nullptr;   // the library's own per-device array: no allocation
-  hipError_t e = spec_sample_scratch(&ws);
+  hipError_t e = spec_sample_scratch(static_cast<hipStream_t>(stream), &ws);
   if (e != hipSuccess) return fail(PKV_EHIP, "scratch address: %s", hipGetErrorString(e));
   e = launch_spec_sample(a, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_EHIP, "speculative sampling launch: %s", hipGetErrorString(e));

@@ -188,8 +188,8 @@ hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s
 size_t spec_sample_workspace_bytes(int32_t batch, int32_t vocab);
 hipError_t launch_spec_sample(const SampleArgs& a, void* workspace, hipStream_t stream);
 // Size of the library's own per-device tile-sum array (allocation-free
-// sampling entry point) and its device address on the current device.
+// sampling entry point) and its device address on the GPU that runs `stream`.
 constexpr size_t kSpecScratchBytes = size_t(4) << 20;
-hipError_t spec_sample_scratch(void** ptr);
+hipError_t spec_sample_scratch(hipStream_t stream, void** ptr);
 
 }  // namespace pkv

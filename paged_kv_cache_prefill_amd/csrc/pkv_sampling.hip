@@ -300,20 +300,33 @@ __global__ __launch_bounds__(kDrawThreads) void spec_draw_kernel(SampleArgs a, c
   }
 }
 
-// Device address of `scratch` on the current device, looked up once per
-// device (with that device current) and kept.
-hipError_t spec_sample_scratch(void** ptr) {
+// Device address of `scratch` on the GPU that runs `stream` (the current
+// device for the null stream): looked up once per device, with that device
+// current (the caller's current device is restored), and kept.
+hipError_t spec_sample_scratch(hipStream_t stream, void** ptr) {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;
   static void* addr[kMaxDevices] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(mu);
   if (addr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
     if (e != hipSuccess) return e;
     addr[dev] = p;
   }
