@@ -700,11 +700,20 @@ std::vector<Staging*> g_staging;
 
 // Upload `bytes` (a multiple of 256) to dst on `stream`: `fill` writes them
 // straight into a free pinned staging buffer, which a copy kernel then reads.
+// Buffers and their events belong to the GPU that runs `stream` (the current
+// device for the null stream), which need not be the current device.
 template <typename Fill>
 pkv_status copy_to_device(void* dst, size_t bytes, const Fill& fill, hipStream_t stream) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return fail(PKV_EHIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    dev = (int)d;
+  }
   std::lock_guard<std::mutex> lock(g_staging_mu);
   Staging* s = nullptr;
   for (Staging* c : g_staging) {
@@ -728,7 +737,14 @@ pkv_status copy_to_device(void* dst, size_t bytes, const Fill& fill, hipStream_t
       delete s;
       return fail(PKV_EHIP, "hipHostGetDevicePointer: %s", hipGetErrorString(e));
     }
-    e = hipEventCreateWithFlags(&s->ev, hipEventDisableTiming);
+    // the event is recorded on `stream`: create it on that stream's device
+    if (dev != cur && (e = hipSetDevice(dev)) == hipSuccess) {
+      e = hipEventCreateWithFlags(&s->ev, hipEventDisableTiming);
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    } else if (dev == cur) {
+      e = hipEventCreateWithFlags(&s->ev, hipEventDisableTiming);
+    }
     if (e != hipSuccess) {
       (void)hipHostFree(s->host);
       delete s;
