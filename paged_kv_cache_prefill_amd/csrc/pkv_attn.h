@@ -79,7 +79,9 @@ __global__ __launch_bounds__(64 * WM * WN, WPE) void attn_kernel(AttnArgs a) {
   // exactly one index, so the one that gets the last index knows every other
   // group of this launch has taken its own and can put the counter back.
   // (short tiles only: the prefill tile's launches with more tasks than slots
-  // are grouped by XCD, and its register budget has no room for this)
+  // keep each (request, kv head)'s tasks on one XCD, whose L2 then serves the
+  // K/V tiles they share; taking tasks in start order across XCDs instead
+  // measured slower there)
   int widx = blockIdx.x;
   if (WN > 1 && a.dyn_base > 0 && widx >= a.dyn_base) {
     __shared__ int lds_task;
